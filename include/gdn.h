@@ -1,0 +1,114 @@
+/*
+ * gdn.h -- C ABI of the gated-delta-rule (Gated DeltaNet) layer core for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation.  "Optimizing on-device inference for Apple Silicon" (Perplexity),
+ * section "Qwen creates three distinct workload shapes", describes the Gated DeltaNet
+ * layer: it packs past context into a fixed-size recurrent state, a learned gate sets
+ * how much of the existing state is kept, a delta update writes in the current token,
+ * and each token depends on the state the previous token left.  Per batch b and value
+ * head h (which reads query/key head h / (Hv / Hk)), with the state S a dv x dk matrix:
+ *
+ *     a_t = exp(g_t)
+ *     S_t = a_t * S_{t-1} * (I - beta_t * k_t k_t^T) + beta_t * v_t k_t^T
+ *     o_t = S_t * q_t
+ *
+ * The same section says a prefill can evaluate this either by scanning tokens while
+ * carrying the state, or by regrouping the updates into blocks that expose matrix
+ * operations and token-level parallelism; gdn_prefill does the latter.  gdn_decode_step
+ * is the one-token update used while generating ("Decode: minimise bytes moved per
+ * token"; the fused "recurrent update" of "Reduce intermediate and state traffic").
+ * Section "Keep the recurrent state on chip" fixes the precision: the state and the
+ * gate are fp32, query/key activations bf16.  Section "Bound temporary memory with
+ * prompt chunking" fixes the hand-off: a prompt split into segments that carry the
+ * recurrent state gives the same output -- pass one call's state_out as the next
+ * call's state_in.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are HIP DEVICE pointers owned by the caller; the library never
+ *     allocates, frees or retains them.  Tensors are dense, contiguous, row-major.
+ *   - q, k, v and o hold elements of type `dtype` (bf16 = 2-byte bfloat16, f32 = float);
+ *     g, beta and the state are always float (fp32).
+ *   - q, k, v, o, state pointers must be 16-byte aligned; g, beta 4-byte aligned.
+ *   - No query scaling is applied and q, k are used as given (callers that want
+ *     L2-normalised q, k normalise them first).  g must be finite (a_t > 0).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work on
+ *     it and return without synchronising; argument errors are reported synchronously,
+ *     before anything is enqueued.  Asynchronous kernel faults surface on the stream.
+ *   - Shapes supported: dk, dv in {32, 64, 128}; Hk >= 1; Hv a multiple of Hk; B >= 1;
+ *     chunk in {16, 32, 64}; any T >= 0 (a final chunk shorter than `chunk` is exact).
+ *   - Thread safety: no global mutable state; concurrent calls on different streams
+ *     with disjoint buffers are safe.
+ *   - Return value: a gdn_status; GDN_OK (0) on success.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,        /* a required pointer is NULL                                  */
+    GDN_ERR_SHAPE = 2,       /* a size is negative / zero where it may not be, or Hv % Hk != 0 */
+    GDN_ERR_UNSUPPORTED = 3, /* dk, dv, chunk or dtype outside the supported set            */
+    GDN_ERR_ALIGN = 4,       /* a pointer violates the alignment rules above                */
+    GDN_ERR_ALIAS = 5,       /* an output overlaps another argument (state_out == state_in is allowed) */
+    GDN_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than gdn_prefill_workspace_bytes  */
+    GDN_ERR_HIP = 7          /* the HIP runtime reported an error while enqueueing          */
+} gdn_status;
+
+/* Bytes of device workspace gdn_prefill needs for these sizes (0 when T == 0).  Returns 0
+ * also for unsupported arguments (gdn_prefill then reports the reason).  The workspace
+ * holds the per-chunk blocks of the blockwise form between its two kernels; its content
+ * on entry is irrelevant and on exit unspecified. */
+size_t gdn_prefill_workspace_bytes(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                                   gdn_dtype dtype);
+
+/* Blockwise (chunked) prefill over T tokens.
+ *   q, k       [B, T, Hk, dk] dtype      v  [B, T, Hv, dv] dtype
+ *   g, beta    [B, T, Hv] float          (log-gate, finite; update strength)
+ *   state_in   [B, Hv, dv, dk] float, or NULL for a zero starting state
+ *   o          [B, T, Hv, dv] dtype      (o_t = S_t q_t, the post-update state read with q_t)
+ *   state_out  [B, Hv, dv, dk] float     (state after token T-1; may equal state_in, which
+ *                                         is then updated in place)
+ *   workspace  device buffer of at least gdn_prefill_workspace_bytes(...) bytes; may be
+ *              NULL only when T == 0.
+ * T == 0 copies state_in (or zeros) to state_out and touches nothing else.
+ * Outputs must not overlap each other, the inputs or the workspace, except
+ * state_out == state_in exactly. */
+gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, const float *state_in, void *o, float *state_out,
+                       int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype dtype,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* One-token recurrent update (decode step), in place or out of place.
+ *   q, k       [B, Hk, dk] dtype         v  [B, Hv, dv] dtype
+ *   g, beta    [B, Hv] float
+ *   state_in   [B, Hv, dv, dk] float (required)
+ *   state_out  [B, Hv, dv, dk] float; may equal state_in (in-place update)
+ *   o          [B, Hv, dv] dtype
+ * Each state element is read once and written once; independent layers can be batched
+ * through B when their states are laid out back to back. */
+gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, const float *state_in, float *state_out, void *o,
+                           int B, int Hk, int Hv, int dk, int dv, gdn_dtype dtype, void *stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *gdn_status_string(gdn_status status);
+
+/* GDN_ABI_VERSION of the built library. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

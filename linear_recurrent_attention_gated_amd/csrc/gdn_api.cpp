@@ -1,0 +1,172 @@
+// gdn_api.cpp -- the C ABI declared in include/gdn.h: synchronous argument validation,
+// workspace carving, and dispatch to the compiled kernel variants.  Nothing here
+// allocates device memory or synchronises the stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+#include "gdn_launch.h"
+
+namespace {
+
+bool supported_dim(int d) { return d == 32 || d == 64 || d == 128; }
+bool supported_chunk(int c) { return c == 16 || c == 32 || c == 64; }
+size_t elem_size(gdn_dtype dt) { return dt == GDN_BF16 ? 2 : 4; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Span {
+    const void* p;
+    size_t n;
+};
+bool overlap(Span a, Span b) {
+    if (!a.p || !b.p || !a.n || !b.n) return false;
+    const uintptr_t x = (uintptr_t)a.p, y = (uintptr_t)b.p;
+    return x < y + b.n && y < x + a.n;
+}
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Workspace regions of the blockwise prefill (see gdn_prefill.h).
+struct Layout {
+    size_t W, Ut, P, KT, gam, total;
+};
+Layout layout(int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype dt) {
+    const size_t es = elem_size(dt);
+    const size_t N = ((size_t)T + chunk - 1) / chunk, Tp = N * (size_t)chunk;
+    Layout L;
+    size_t off = 0;
+    L.W = off;   off = round_up(off + (size_t)B * Hv * Tp * dk * es, 256);
+    L.Ut = off;  off = round_up(off + (size_t)B * Hv * Tp * dv * es, 256);
+    L.P = off;   off = round_up(off + (size_t)B * Hv * Tp * chunk * es, 256);
+    L.KT = off;  off = round_up(off + (size_t)B * Hk * Tp * dk * es, 256);
+    L.gam = off; off = round_up(off + (size_t)B * Hv * Tp * sizeof(float), 256);
+    L.total = off;
+    return L;
+}
+
+gdn_status shape_check(int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype dt,
+                       bool prefill) {
+    if (B < 1 || T < 0 || Hk < 1 || Hv < 1 || Hv % Hk != 0) return GDN_ERR_SHAPE;
+    if (dt != GDN_BF16 && dt != GDN_F32) return GDN_ERR_UNSUPPORTED;
+    if (!supported_dim(dk) || !supported_dim(dv)) return GDN_ERR_UNSUPPORTED;
+    if (prefill && !supported_chunk(chunk)) return GDN_ERR_UNSUPPORTED;
+    // keep every launch dimension and 32-bit intermediate in range
+    if ((int64_t)B * Hv * (dv / 16) > INT32_MAX / 2 || (int64_t)T > (int64_t)INT32_MAX / 4)
+        return GDN_ERR_SHAPE;
+    if (prefill && (Hv > 65535 || B > 65535)) return GDN_ERR_SHAPE;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_prefill_workspace_bytes(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                                   gdn_dtype dtype) {
+    if (shape_check(B, T, Hk, Hv, dk, dv, chunk, dtype, true) != GDN_OK || T == 0) return 0;
+    return layout(B, T, Hk, Hv, dk, dv, chunk, dtype).total;
+}
+
+gdn_status gdn_prefill(const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, const float* state_in, void* o, float* state_out,
+                       int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    const gdn_status sc = shape_check(B, T, Hk, Hv, dk, dv, chunk, dtype, true);
+    if (sc != GDN_OK) return sc;
+    if (!state_out) return GDN_ERR_NULL;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+    const size_t es = elem_size(dtype);
+    const size_t nqk = (size_t)B * T * Hk * dk * es, nv = (size_t)B * T * Hv * dv * es;
+    const size_t ng = (size_t)B * T * Hv * sizeof(float);
+    const size_t ns = (size_t)B * Hv * dv * dk * sizeof(float);
+    if (!aligned(state_out, 16) || (state_in && !aligned(state_in, 16))) return GDN_ERR_ALIGN;
+    if (T > 0) {
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+            !aligned(g, 4) || !aligned(beta, 4))
+            return GDN_ERR_ALIGN;
+    }
+    const Span sq{q, T ? nqk : 0}, sk{k, T ? nqk : 0}, sv{v, T ? nv : 0}, sg{g, T ? ng : 0},
+        sb{beta, T ? ng : 0}, si{state_in, ns}, so{o, T ? nv : 0}, ss{state_out, ns},
+        sw{workspace, T ? workspace_bytes : 0};
+    for (Span in : {sq, sk, sv, sg, sb, si, sw})
+        if (overlap(so, in)) return GDN_ERR_ALIAS;
+    for (Span in : {sq, sk, sv, sg, sb, sw, so})
+        if (overlap(ss, in)) return GDN_ERR_ALIAS;
+    if (state_in && state_in != state_out && overlap(ss, si)) return GDN_ERR_ALIAS;
+    for (Span in : {sq, sk, sv, sg, sb, si})
+        if (overlap(sw, in)) return GDN_ERR_ALIAS;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (T == 0) {
+        return gdn::copy_state(state_in, state_out, (size_t)B * Hv * dv * dk, st) == hipSuccess
+                   ? GDN_OK : GDN_ERR_HIP;
+    }
+    const Layout L = layout(B, T, Hk, Hv, dk, dv, chunk, dtype);
+    if (!workspace || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
+
+    gdn::PrefillParams p;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.state_in = state_in;
+    p.o = o; p.state_out = state_out;
+    char* ws = static_cast<char*>(workspace);
+    p.W = ws + L.W; p.Ut = ws + L.Ut; p.P = ws + L.P; p.KT = ws + L.KT;
+    p.gam = reinterpret_cast<float*>(ws + L.gam);
+    p.B = B; p.T = T; p.Hk = Hk; p.Hv = Hv; p.N = (T + chunk - 1) / chunk;
+
+    hipError_t e = hipErrorInvalidValue;
+    if (dtype == GDN_BF16) {
+        if (chunk == 16) e = gdn::prefill_bf16_c16(dk, dv, p, st);
+        else if (chunk == 32) e = gdn::prefill_bf16_c32(dk, dv, p, st);
+        else e = gdn::prefill_bf16_c64(dk, dv, p, st);
+    } else {
+        if (chunk == 16) e = gdn::prefill_f32_c16(dk, dv, p, st);
+        else if (chunk == 32) e = gdn::prefill_f32_c32(dk, dv, p, st);
+        else e = gdn::prefill_f32_c64(dk, dv, p, st);
+    }
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const float* state_in, float* state_out, void* o,
+                           int B, int Hk, int Hv, int dk, int dv, gdn_dtype dtype, void* stream) {
+    const gdn_status sc = shape_check(B, 1, Hk, Hv, dk, dv, 16, dtype, false);
+    if (sc != GDN_OK) return sc;
+    if (!q || !k || !v || !g || !beta || !state_in || !state_out || !o) return GDN_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(state_in, 16) || !aligned(state_out, 16) || !aligned(g, 4) || !aligned(beta, 4))
+        return GDN_ERR_ALIGN;
+    const size_t es = elem_size(dtype);
+    const Span sq{q, (size_t)B * Hk * dk * es}, sk{k, (size_t)B * Hk * dk * es},
+        sv{v, (size_t)B * Hv * dv * es}, sg{g, (size_t)B * Hv * 4}, sb{beta, (size_t)B * Hv * 4},
+        si{state_in, (size_t)B * Hv * dv * dk * 4}, ss{state_out, (size_t)B * Hv * dv * dk * 4},
+        so{o, (size_t)B * Hv * dv * es};
+    for (Span in : {sq, sk, sv, sg, sb, si, ss})
+        if (overlap(so, in)) return GDN_ERR_ALIAS;
+    for (Span in : {sq, sk, sv, sg, sb})
+        if (overlap(ss, in)) return GDN_ERR_ALIAS;
+    if (state_in != state_out && overlap(ss, si)) return GDN_ERR_ALIAS;
+
+    gdn::DecodeParams p;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.state_in = state_in;
+    p.state_out = state_out; p.o = o; p.B = B; p.Hk = Hk; p.Hv = Hv;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const hipError_t e = dtype == GDN_BF16 ? gdn::decode_bf16(dk, dv, p, st) : gdn::decode_f32(dk, dv, p, st);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+const char* gdn_status_string(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_NULL: return "a required pointer is NULL";
+        case GDN_ERR_SHAPE: return "invalid sizes (B, T, Hk, Hv) or Hv not a multiple of Hk";
+        case GDN_ERR_UNSUPPORTED: return "unsupported dk, dv, chunk or dtype";
+        case GDN_ERR_ALIGN: return "misaligned pointer";
+        case GDN_ERR_ALIAS: return "an output overlaps another argument";
+        case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+        case GDN_ERR_HIP: return "HIP runtime error while enqueueing";
+    }
+    return "unknown status";
+}
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+}  // extern "C"

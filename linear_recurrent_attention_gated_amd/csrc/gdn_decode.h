@@ -1,0 +1,108 @@
+// gdn_decode.h -- one-token recurrent update (decode step) of the gated delta rule.
+//
+// "Optimizing on-device inference for Apple Silicon", section "Decode: minimise bytes
+// moved per token": at batch 1 the step is bound by the bytes it moves, and section
+// "Reduce intermediate and state traffic" fuses the recurrent update into one kernel
+// that keeps temporaries in registers.  Here the state is the traffic: every fp32
+// element is read once and written once, nothing else touches memory in bulk.
+//
+// Per state row i (rows evolve independently):
+//   s_k = S_i . k,  s_q = S_i . q                  (cross-lane reductions)
+//   delta_i = beta (v_i - a s_k)                   a = exp(g)
+//   S_i <- a S_i + delta_i k^T
+//   o_i = S_i(new) . q = a s_q + delta_i (k . q)
+//
+// Mapping: a row of dk floats is read by dk/4 consecutive lanes as 16-byte vectors, so
+// a wavefront reads 1 KiB of contiguous state per instruction; each thread keeps NIT
+// rows in flight before it reduces.  No matrix cores: the arithmetic is 3 FMAs per state
+// element against 8 bytes of traffic.
+#pragma once
+
+#include "gdn_device.h"
+
+namespace gdn {
+
+struct DecodeParams {
+    const void* q;        // [B][Hk][DK]
+    const void* k;        // [B][Hk][DK]
+    const void* v;        // [B][Hv][DV]
+    const float* g;       // [B][Hv]
+    const float* beta;    // [B][Hv]
+    const float* state_in;
+    float* state_out;     // [B][Hv][DV][DK]
+    void* o;              // [B][Hv][DV]
+    int B, Hk, Hv;
+};
+
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+    using X = Elem<E>;
+    constexpr int LPR = DK / 4;
+    constexpr int RIT = 256 / LPR;
+    constexpr int RPB = (2 * RIT < DV) ? 2 * RIT : DV;
+    constexpr int NIT = RPB / RIT;
+    constexpr int NBLK = DV / RPB;
+    static_assert(RIT <= DV && NIT * RIT == RPB && NBLK * RPB == DV, "decode tiling");
+
+    const int blk = blockIdx.x % NBLK;
+    const int bh = blockIdx.x / NBLK;
+    const int h = bh % p.Hv, b = bh / p.Hv;
+    const int hk = h / (p.Hv / p.Hk);
+    const int tid = threadIdx.x;
+    const int sub = tid % LPR, rloc = tid / LPR;
+    const int c0 = sub * 4;
+
+    const E* kp = reinterpret_cast<const E*>(p.k) + ((size_t)b * p.Hk + hk) * DK + c0;
+    const E* qp = reinterpret_cast<const E*>(p.q) + ((size_t)b * p.Hk + hk) * DK + c0;
+    float kk[4], qq[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { kk[e] = X::to_f(kp[e]); qq[e] = X::to_f(qp[e]); }
+
+    const size_t row0 = ((size_t)b * p.Hv + h) * DV + (size_t)blk * RPB + rloc;
+    float4 s[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it)
+        s[it] = *reinterpret_cast<const float4*>(p.state_in + (row0 + (size_t)it * RIT) * DK + c0);
+
+    const float a = expf(p.g[(size_t)b * p.Hv + h]);
+    const float bt = p.beta[(size_t)b * p.Hv + h];
+    float kq = kk[0] * qq[0] + kk[1] * qq[1] + kk[2] * qq[2] + kk[3] * qq[3];
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) kq += __shfl_xor(kq, off, 64);
+
+    const E* vp = reinterpret_cast<const E*>(p.v);
+    E* op = reinterpret_cast<E*>(p.o);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        float sk = s[it].x * kk[0] + s[it].y * kk[1] + s[it].z * kk[2] + s[it].w * kk[3];
+        float sq = s[it].x * qq[0] + s[it].y * qq[1] + s[it].z * qq[2] + s[it].w * qq[3];
+#pragma unroll
+        for (int off = LPR / 2; off > 0; off >>= 1) {
+            sk += __shfl_xor(sk, off, 64);
+            sq += __shfl_xor(sq, off, 64);
+        }
+        const size_t row = row0 + (size_t)it * RIT;
+        const float vi = X::to_f(vp[row]);
+        const float delta = bt * (vi - a * sk);
+        float4 ns;
+        ns.x = a * s[it].x + delta * kk[0];
+        ns.y = a * s[it].y + delta * kk[1];
+        ns.z = a * s[it].z + delta * kk[2];
+        ns.w = a * s[it].w + delta * kk[3];
+        *reinterpret_cast<float4*>(p.state_out + row * DK + c0) = ns;
+        if (sub == 0) op[row] = X::from_f(a * sq + delta * kq);
+    }
+}
+
+template <typename E, int DK, int DV>
+inline hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+    constexpr int LPR = DK / 4;
+    constexpr int RIT = 256 / LPR;
+    constexpr int RPB = (2 * RIT < DV) ? 2 * RIT : DV;
+    constexpr int NBLK = DV / RPB;
+    dim3 grid((unsigned)(p.B * p.Hv * NBLK));
+    decode_kernel<E, DK, DV><<<grid, 256, 0, stream>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

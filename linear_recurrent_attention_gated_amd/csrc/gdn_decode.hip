@@ -1,0 +1,28 @@
+// gdn_decode.hip -- decode-step variants and the T == 0 state copy.
+#include "gdn_launch.h"
+
+namespace gdn {
+
+template <int DK, int DV>
+static hipError_t run_bf16(const DecodeParams& p, hipStream_t s) { return launch_decode<bf16_t, DK, DV>(p, s); }
+template <int DK, int DV>
+static hipError_t run_f32(const DecodeParams& p, hipStream_t s) { return launch_decode<float, DK, DV>(p, s); }
+
+hipError_t decode_bf16(int dk, int dv, const DecodeParams& p, hipStream_t s) { GDN_SWITCH_DIMS(dk, dv, run_bf16, p, s) }
+hipError_t decode_f32(int dk, int dv, const DecodeParams& p, hipStream_t s) { GDN_SWITCH_DIMS(dk, dv, run_f32, p, s) }
+
+// Grid-stride copy (or zero fill when in == nullptr) of n floats.
+__global__ __launch_bounds__(256) void copy_state_kernel(const float* in, float* out, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+        out[i] = in ? in[i] : 0.f;
+}
+
+hipError_t copy_state(const float* in, float* out, size_t n, hipStream_t s) {
+    if (n == 0 || in == out) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    copy_state_kernel<<<dim3((unsigned)blocks), 256, 0, s>>>(in, out, n);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,118 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every entry point that
+include/gdn.h declares, reports its ABI version, sizes the workspace, and rejects
+bad arguments synchronously -- before anything is enqueued -- with the documented
+status codes.  No call here reaches a kernel launch (all arguments are invalid in
+at least one way, and validation runs first), so no GPU is needed."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_recurrent_attention_gated_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = gdn.lib()
+    declared = header_functions()
+    assert set(declared) == set(gdn.EXPORTS), declared
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert gdn.gdn_abi_version() == 1
+    for code in range(8):
+        assert gdn.gdn_status_string(code)
+    assert gdn.gdn_status_string(99) == "unknown status"
+
+
+def test_workspace_bytes():
+    # prefill at T=4096, Hk=16, Hv=32, dk=dv=128, chunk 64, bf16:
+    # W, Ut: 32*4096*128*2 each; P: 32*4096*64*2; K^T: 16*4096*128*2; gamma: 32*4096*4
+    expect = 2 * 32 * 4096 * 128 * 2 + 32 * 4096 * 64 * 2 + 16 * 4096 * 128 * 2 + 32 * 4096 * 4
+    assert gdn.gdn_prefill_workspace_bytes(1, 4096, 16, 32, 128, 128, 64, 0) == expect
+    assert gdn.gdn_prefill_workspace_bytes(1, 0, 16, 32, 128, 128, 64, 0) == 0
+    assert gdn.gdn_prefill_workspace_bytes(1, 64, 16, 32, 96, 128, 64, 0) == 0     # unsupported
+    # a ragged tail rounds up to whole chunks
+    assert gdn.gdn_prefill_workspace_bytes(1, 65, 1, 1, 32, 32, 16, 1) == \
+        gdn.gdn_prefill_workspace_bytes(1, 80, 1, 1, 32, 32, 16, 1)
+
+
+# Fake, well-separated "device" addresses: never dereferenced, validation rejects first.
+BASE = 1 << 40
+MB = 1 << 20
+
+
+def _prefill(**kw):
+    a = dict(q=BASE, k=BASE + 10 * MB, v=BASE + 20 * MB, g=BASE + 40 * MB, beta=BASE + 41 * MB,
+             state_in=BASE + 50 * MB, o=BASE + 60 * MB, state_out=BASE + 80 * MB, B=1, T=64, Hk=2,
+             Hv=4, dk=32, dv=32, chunk=16, dtype=0, ws=BASE + 100 * MB, ws_bytes=0, stream=None)
+    a.update(kw)
+    if "ws_bytes" not in kw:
+        a["ws_bytes"] = gdn.gdn_prefill_workspace_bytes(a["B"], a["T"], a["Hk"], a["Hv"], a["dk"],
+                                                        a["dv"], a["chunk"], a["dtype"])
+    return gdn.lib().gdn_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state_in"], a["o"],
+                                 a["state_out"], a["B"], a["T"], a["Hk"], a["Hv"], a["dk"], a["dv"],
+                                 a["chunk"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def _decode(**kw):
+    a = dict(q=BASE, k=BASE + MB, v=BASE + 2 * MB, g=BASE + 3 * MB, beta=BASE + 4 * MB,
+             state_in=BASE + 10 * MB, state_out=BASE + 10 * MB, o=BASE + 30 * MB, B=1, Hk=2, Hv=4,
+             dk=32, dv=32, dtype=0, stream=None)
+    a.update(kw)
+    return gdn.lib().gdn_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state_in"],
+                                     a["state_out"], a["o"], a["B"], a["Hk"], a["Hv"], a["dk"],
+                                     a["dv"], a["dtype"], a["stream"])
+
+
+# Each case breaks exactly one rule; the rest of the call is valid.
+PREFILL_ERRORS = [
+    (dict(q=None), 1), (dict(state_out=None), 1), (dict(beta=None), 1),
+    (dict(Hv=3), 2), (dict(B=0), 2), (dict(T=-1), 2), (dict(Hk=0), 2),
+    (dict(dk=48), 3), (dict(dv=256), 3), (dict(chunk=128), 3), (dict(chunk=8), 3), (dict(dtype=7), 3),
+    (dict(q=BASE + 2), 4), (dict(o=BASE + 60 * MB + 8), 4), (dict(g=BASE + 40 * MB + 2), 4),
+    (dict(state_in=BASE + 50 * MB + 4), 4),
+    (dict(o=BASE + 10 * MB), 5),                         # o overlaps k
+    (dict(state_out=BASE + 60 * MB + 4096), 5),          # state_out overlaps o
+    (dict(state_out=BASE + 50 * MB + 4096), 5),          # partial overlap with state_in
+    (dict(ws=BASE + 20 * MB), 5),                        # workspace overlaps v
+    (dict(ws_bytes=1024), 6), (dict(ws=None), 6),
+]
+
+
+@pytest.mark.parametrize("kw,code", PREFILL_ERRORS)
+def test_prefill_rejects(kw, code):
+    assert _prefill(**kw) == code
+
+
+DECODE_ERRORS = [
+    (dict(state_in=None), 1), (dict(o=None), 1),
+    (dict(Hv=5), 2), (dict(B=0), 2),
+    (dict(dk=16), 3), (dict(dtype=2), 3),
+    (dict(k=BASE + MB + 4), 4), (dict(state_out=BASE + 12 * MB + 8), 4),
+    (dict(o=BASE + 2 * MB), 5),                          # o overlaps v
+    (dict(state_out=BASE + 10 * MB + 1024), 5),          # partial state overlap
+    (dict(state_out=BASE + 64), 5),                      # state_out overlaps q
+]
+
+
+@pytest.mark.parametrize("kw,code", DECODE_ERRORS)
+def test_decode_rejects(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_python_binding_raises_with_status():
+    with pytest.raises(gdn.GdnError) as ei:
+        raise gdn.GdnError("gdn_prefill", 5)
+    assert "GDN_ERR_ALIAS" in str(ei.value)
