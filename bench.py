@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated-delta-rule layer core on one MI355X.
+
+One step = one pass over the whole hot path on synthetic inputs already resident
+in GPU memory:
+  * a blockwise prefill of T = 4096 tokens (B = 1, 16 query/key heads shared 2:1 by
+    32 value heads, dk = dv = 128, chunk 64, bf16 q/k/v/o, fp32 gates and state,
+    zero starting state), run as its two stages (gdn_prefill_prepare, then
+    gdn_prefill_scan) so each kernel is timed with HIP events on its stream;
+  * one decode token through 30 independent recurrent layers (fp32 states of
+    32 x 128 x 128, N(0, 0.1^2)), as 30 back-to-back B = 1 gdn_decode_step calls.
+Inputs rotate over several buffer sets so that every step reads cold memory
+(the sets together exceed the 256 MB last-level cache).
+
+value = prefill tokens per second (T / mean event time of the two prefill
+kernels).  The JSON line also carries the decode figures, the roofline of the
+prefill path and of the decode kernel, and the CPU oracle timed on the host on
+the same prefill workload (whose output doubles as a parity check of the GPU
+output).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+LAYERS = 30
+
+# Algorithmic bytes of the prefill per token at these head shapes: q and k (16 heads x 128 x
+# bf16 each), v and o (32 heads x 128 x bf16 each), g and beta (32 heads x fp32 each).
+PREFILL_BYTES_PER_TOKEN = 16 * 128 * 2 * 2 + 32 * 128 * 2 * 2 + 32 * 4 * 2     # 24,832
+STATE_BYTES = 32 * 128 * 128 * 4                                               # 2 MiB
+# Matrix-core FLOPs of the blockwise form per token per value head (chunk C = 64, dk = dv = 128,
+# the two Gram blocks shared by the two value heads of a key head):
+#   2 * [C dk (Grams) + C dk (W) + 2 C dv (U~, P U) + 3 dk dv (W S^T, Q S^T, U^T K) + C^2 / 6 (inverse)]
+PREFILL_FLOP_PER_TOKEN_HEAD = 2 * (64 * 128 + 64 * 128 + 2 * 64 * 128 + 3 * 128 * 128 + 64 * 64 / 6)
+# Decode: each fp32 state element read once and written once, plus q, k, v, g, beta, o.
+DECODE_BYTES_PER_LAYER = 2 * STATE_BYTES + PREFILL_BYTES_PER_TOKEN                  # 4,219,136
+
+SOURCES = ["linear_recurrent_attention_gated_amd/csrc/" + f for f in
+           ("gdn_device.h", "gdn_prefill.h", "gdn_decode.h", "gdn_launch.h", "gdn_api.cpp",
+            "gdn_prefill_inst.hip", "gdn_decode.hip")]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/traffic.json), used only
+    while the kernel sources are unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            doc = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if doc.get("source_hash") != kernel_source_hash():
+        return None
+    return doc
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sets", type=int, default=6, help="rotating input buffer sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=None)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the gated-delta-rule core is built and measured "
+              "on a single MI355X; runs on more than one GPU are not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from linear_recurrent_attention_gated_amd import gdn
+    from linear_recurrent_attention_gated_amd.inputs import (PREFILL_4K, decode_inputs,
+                                                             workload_inputs)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = gdn.lib()
+    w = PREFILL_4K
+    B, T, Hk, Hv, dk, dv, C = w.B, w.T, w.Hk, w.Hv, w.dk, w.dv, w.chunk
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    # -- inputs: one seeded draw, copied into rotating buffer sets -----------------------------
+    host = workload_inputs(w, torch.bfloat16)
+    ws_bytes = gdn.gdn_prefill_workspace_bytes(B, T, Hk, Hv, dk, dv, C, torch.bfloat16)
+    dec_host = [decode_inputs(l) for l in range(LAYERS)]
+    dec_cat = {k: torch.cat([d[k] for d in dec_host]).contiguous() for k in dec_host[0]}
+    sets = []
+    for _ in range(args.sets):
+        s = {k: host[k].to(dev) for k in ("q", "k", "v", "g", "beta")}
+        s["o"] = torch.empty((B, T, Hv, dv), dtype=torch.bfloat16, device=dev)
+        s["state_out"] = torch.empty((B, Hv, dv, dk), dtype=torch.float32, device=dev)
+        s["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        dd = {k: v.to(dev) for k, v in dec_cat.items()}
+        dd["o"] = torch.empty((LAYERS, Hv, dv), dtype=torch.bfloat16, device=dev)
+        s["dec"] = dd
+        sets.append(s)
+    torch.cuda.synchronize()
+
+    def pf_args(s):
+        return (s["q"].data_ptr(), s["k"].data_ptr(), s["v"].data_ptr(), s["g"].data_ptr(),
+                s["beta"].data_ptr(), None, s["o"].data_ptr(), s["state_out"].data_ptr(),
+                B, T, Hk, Hv, dk, dv, C, gdn.GDN_BF16, s["ws"].data_ptr(), ws_bytes, sh)
+
+    def dec_args(s, l0, nb):
+        d = s["dec"]
+        st = d["state"][l0].data_ptr()
+        return (d["q"][l0].data_ptr(), d["k"][l0].data_ptr(), d["v"][l0].data_ptr(),
+                d["g"][l0].data_ptr(), d["beta"][l0].data_ptr(), st, st, d["o"][l0].data_ptr(),
+                nb, Hk, Hv, dk, dv, gdn.GDN_BF16, sh)
+
+    PF = [pf_args(s) for s in sets]
+    DEC = [[dec_args(s, l, 1) for l in range(LAYERS)] for s in sets]
+    DEC_B = [dec_args(s, 0, LAYERS) for s in sets]
+
+    def check(rc, fn):
+        if rc != 0:
+            raise gdn.GdnError(fn, rc)
+
+    nsteps = args.warmup + args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nsteps)]
+
+    def step(i):
+        j = i % len(sets)
+        e = ev[i]
+        e[0].record(stream)
+        check(lib.gdn_prefill_prepare(*PF[j]), "gdn_prefill_prepare")
+        e[1].record(stream)
+        check(lib.gdn_prefill_scan(*PF[j]), "gdn_prefill_scan")
+        e[2].record(stream)
+        for a in DEC[j]:
+            check(lib.gdn_decode_step(*a), "gdn_decode_step")
+        e[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, nsteps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timed = ev[args.warmup:]
+    t_intra = np.array([e[0].elapsed_time(e[1]) for e in timed]) * 1e3   # us
+    t_inter = np.array([e[1].elapsed_time(e[2]) for e in timed]) * 1e3
+    t_dec = np.array([e[2].elapsed_time(e[3]) for e in timed]) * 1e3
+    t_prefill = t_intra + t_inter
+
+    # -- decode, all 30 layers as one batched launch (layers are independent) -------------------
+    evb = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps + 3):
+        j = i % len(sets)
+        if i >= 3:
+            evb[i - 3][0].record(stream)
+        check(lib.gdn_decode_step(*DEC_B[j]), "gdn_decode_step")
+        if i >= 3:
+            evb[i - 3][1].record(stream)
+    torch.cuda.synchronize()
+    t_dec_b = np.array([a.elapsed_time(b) for a, b in evb]) * 1e3
+
+    # -- warm-cache prefill (same buffers every time), secondary -------------------------------
+    evw = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps + 2):
+        if i >= 2:
+            evw[i - 2][0].record(stream)
+        check(lib.gdn_prefill_prepare(*PF[0]), "gdn_prefill_prepare")
+        if i >= 2:
+            evw[i - 2][1].record(stream)
+        check(lib.gdn_prefill_scan(*PF[0]), "gdn_prefill_scan")
+        if i >= 2:
+            evw[i - 2][2].record(stream)
+    torch.cuda.synchronize()
+    tw_intra = np.array([e[0].elapsed_time(e[1]) for e in evw]) * 1e3
+    tw_inter = np.array([e[1].elapsed_time(e[2]) for e in evw]) * 1e3
+
+    mean_pf = float(t_prefill.mean())
+    value = T / (mean_pf * 1e-6)
+    pf_bytes = T * PREFILL_BYTES_PER_TOKEN + STATE_BYTES        # zero start state: state_out only
+    pf_flops = T * Hv * PREFILL_FLOP_PER_TOKEN_HEAD
+    achieved = pf_bytes / (mean_pf * 1e-6) / 1e9
+    traffic_doc = load_traffic()
+    traffic = None
+    if traffic_doc:
+        traffic = traffic_doc.get("prefill_bytes_per_launch")
+
+    dec_layer_us = float(t_dec.mean()) / LAYERS
+    dec_b_us = float(t_dec_b.mean())
+    dec_bytes_b = LAYERS * DECODE_BYTES_PER_LAYER
+    dec_gbs_b = dec_bytes_b / (dec_b_us * 1e-6) / 1e9
+    dec_gbs_loop = dec_bytes_b / (float(t_dec.mean()) * 1e-6) / 1e9
+
+    out = {
+        "metric": "GDN prefill tokens/s @T=4096 (MFMA %peak); decode-step us/token (HBM GB/s)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "T": T, "Hk": Hk, "Hv": Hv, "dk": dk, "dv": dv,
+                   "chunk": C, "state": "fp32, zero start", "decode_layers": LAYERS,
+                   "input_sets": args.sets},
+        "prefill": {
+            "us_mean": round(mean_pf, 2), "us_median": round(float(np.median(t_prefill)), 2),
+            "us_p10": round(float(np.percentile(t_prefill, 10)), 2),
+            "us_p90": round(float(np.percentile(t_prefill, 90)), 2),
+            "intra_chunk_us": round(float(t_intra.mean()), 2),
+            "inter_chunk_us": round(float(t_inter.mean()), 2),
+            "warm_intra_chunk_us": round(float(tw_intra.mean()), 2),
+            "warm_inter_chunk_us": round(float(tw_inter.mean()), 2),
+            "mfma_tflops": round(pf_flops / (mean_pf * 1e-6) / 1e12, 2),
+            "mfma_frac": round(pf_flops / (mean_pf * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        },
+        "roofline": {
+            "kernel": "gdn_prefill = intra_chunk_kernel + inter_chunk_kernel (sum of their mean "
+                      "event-timed durations)",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": pf_bytes,
+        },
+        "decode": {
+            "us_per_token_looped": round(float(t_dec.mean()), 2),
+            "us_per_layer_looped": round(dec_layer_us, 3),
+            "hbm_gbs_looped": round(dec_gbs_loop, 1),
+            "us_per_token_batched": round(dec_b_us, 2),
+            "hbm_gbs_batched": round(dec_gbs_b, 1),
+            "roofline": {"kernel": "decode_kernel, one launch over the 30 layers (B=30)",
+                         "bound": "hbm", "achieved": round(dec_gbs_b, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(dec_gbs_b / HBM_PEAK_GBS, 4),
+                         "traffic": traffic_doc.get("decode_b30_bytes_per_launch") if traffic_doc else None,
+                         "algorithmic_bytes_per_launch": dec_bytes_b},
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        from oracle import gdn_oracle as orc
+        try:
+            ncpu = len(os.sched_getaffinity(0))
+        except AttributeError:
+            ncpu = os.cpu_count() or 1
+        threads = args.cpu_threads or max(1, min(16, ncpu))
+        f = lambda t: t.float().numpy()  # noqa: E731
+        qa, ka, va, ga, ba = (f(host[k]) for k in ("q", "k", "v", "g", "beta"))
+        c0 = time.perf_counter()
+        o_ref, s_ref = orc.seq(qa, ka, va, ga, ba, nthreads=threads, rows_per_item=8)
+        cpu_s = time.perf_counter() - c0
+        o_gpu = sets[0]["o"].float().cpu().numpy()
+        s_gpu = sets[0]["state_out"].cpu().numpy()
+        err = lambda x, r: float(np.max(np.abs(x - r)) / np.max(np.abs(r)))  # noqa: E731
+        out["cpu_baseline"] = {"value": round(T / cpu_s, 1), "unit": "tokens/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"the full prefill workload (T={T}, all {Hv} value heads), "
+                                         f"fp64 token-by-token scan, {threads} threads, "
+                                         f"{cpu_s:.2f} s"}
+        out["parity_vs_oracle"] = {"o": err(o_gpu, o_ref), "state": err(s_gpu, s_ref),
+                                   "tol_o": 2e-2, "tol_state": 1e-2}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -89,6 +89,29 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
                        int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype dtype,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* The two stages of gdn_prefill, for callers that schedule them separately (for example
+ * to overlap the state-independent stage of one segment with other work, or to time each
+ * stage).  Same arguments and rules as gdn_prefill; gdn_prefill == prepare then scan on
+ * one stream with one workspace.
+ *   gdn_prefill_prepare: the state-independent per-chunk blocks (decay-masked Gram, the
+ *     unit-triangular inverse, the W / U~ blocks, the masked query-key block), written to
+ *     the workspace.  Reads q, k, v, g, beta; ignores state_in, o and state_out (they
+ *     still take part in the overlap checks).
+ *   gdn_prefill_scan: carries the state across the chunks in order and writes o and
+ *     state_out.  Reads q, state_in and what gdn_prefill_prepare left in the workspace
+ *     for the same q, k, v, g, beta and sizes; the workspace must not be modified in
+ *     between.  T == 0: state copy, as gdn_prefill. */
+gdn_status gdn_prefill_prepare(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const float *state_in, void *o,
+                               float *state_out, int B, int T, int Hk, int Hv, int dk, int dv,
+                               int chunk, gdn_dtype dtype, void *workspace,
+                               size_t workspace_bytes, void *stream);
+gdn_status gdn_prefill_scan(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const float *state_in, void *o, float *state_out,
+                            int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                            gdn_dtype dtype, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
 /* One-token recurrent update (decode step), in place or out of place.
  *   q, k       [B, Hk, dk] dtype         v  [B, Hv, dv] dtype
  *   g, beta    [B, Hv] float

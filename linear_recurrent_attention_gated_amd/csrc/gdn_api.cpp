@@ -66,10 +66,14 @@ size_t gdn_prefill_workspace_bytes(int B, int T, int Hk, int Hv, int dk, int dv,
     return layout(B, T, Hk, Hv, dk, dv, chunk, dtype).total;
 }
 
-gdn_status gdn_prefill(const void* q, const void* k, const void* v, const float* g,
-                       const float* beta, const float* state_in, void* o, float* state_out,
-                       int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype dtype,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+gdn_status prefill_stages(const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const float* state_in, void* o, float* state_out,
+                          int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype dtype,
+                          void* workspace, size_t workspace_bytes, void* stream, int stages) {
     const gdn_status sc = shape_check(B, T, Hk, Hv, dk, dv, chunk, dtype, true);
     if (sc != GDN_OK) return sc;
     if (!state_out) return GDN_ERR_NULL;
@@ -97,6 +101,7 @@ gdn_status gdn_prefill(const void* q, const void* k, const void* v, const float*
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (T == 0) {
+        if (!(stages & 2)) return GDN_OK;
         return gdn::copy_state(state_in, state_out, (size_t)B * Hv * dv * dk, st) == hipSuccess
                    ? GDN_OK : GDN_ERR_HIP;
     }
@@ -114,15 +119,45 @@ gdn_status gdn_prefill(const void* q, const void* k, const void* v, const float*
 
     hipError_t e = hipErrorInvalidValue;
     if (dtype == GDN_BF16) {
-        if (chunk == 16) e = gdn::prefill_bf16_c16(dk, dv, p, st);
-        else if (chunk == 32) e = gdn::prefill_bf16_c32(dk, dv, p, st);
-        else e = gdn::prefill_bf16_c64(dk, dv, p, st);
+        if (chunk == 16) e = gdn::prefill_bf16_c16(dk, dv, p, stages, st);
+        else if (chunk == 32) e = gdn::prefill_bf16_c32(dk, dv, p, stages, st);
+        else e = gdn::prefill_bf16_c64(dk, dv, p, stages, st);
     } else {
-        if (chunk == 16) e = gdn::prefill_f32_c16(dk, dv, p, st);
-        else if (chunk == 32) e = gdn::prefill_f32_c32(dk, dv, p, st);
-        else e = gdn::prefill_f32_c64(dk, dv, p, st);
+        if (chunk == 16) e = gdn::prefill_f32_c16(dk, dv, p, stages, st);
+        else if (chunk == 32) e = gdn::prefill_f32_c32(dk, dv, p, stages, st);
+        else e = gdn::prefill_f32_c64(dk, dv, p, stages, st);
     }
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill(const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, const float* state_in, void* o, float* state_out,
+                       int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
+                          dtype, workspace, workspace_bytes, stream, 3);
+}
+
+gdn_status gdn_prefill_prepare(const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, const float* state_in, void* o,
+                               float* state_out, int B, int T, int Hk, int Hv, int dk, int dv,
+                               int chunk, gdn_dtype dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
+                          dtype, workspace, workspace_bytes, stream, 1);
+}
+
+gdn_status gdn_prefill_scan(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const float* state_in, void* o, float* state_out,
+                            int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                            gdn_dtype dtype, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
+                          dtype, workspace, workspace_bytes, stream, 2);
 }
 
 gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const float* g,

@@ -8,14 +8,15 @@
 
 namespace gdn {
 
-// One entry per (element type, chunk); each switches on (dk, dv).  Return hipErrorInvalidValue
+// One entry per (element type, chunk); each switches on (dk, dv).  `stages`: bit 1 runs the
+// intra-chunk kernel, bit 2 the inter-chunk kernel.  Return hipErrorInvalidValue
 // for a (dk, dv) pair that was not compiled (the API validates before calling).
-hipError_t prefill_bf16_c16(int dk, int dv, const PrefillParams& p, hipStream_t s);
-hipError_t prefill_bf16_c32(int dk, int dv, const PrefillParams& p, hipStream_t s);
-hipError_t prefill_bf16_c64(int dk, int dv, const PrefillParams& p, hipStream_t s);
-hipError_t prefill_f32_c16(int dk, int dv, const PrefillParams& p, hipStream_t s);
-hipError_t prefill_f32_c32(int dk, int dv, const PrefillParams& p, hipStream_t s);
-hipError_t prefill_f32_c64(int dk, int dv, const PrefillParams& p, hipStream_t s);
+hipError_t prefill_bf16_c16(int dk, int dv, const PrefillParams& p, int stages, hipStream_t s);
+hipError_t prefill_bf16_c32(int dk, int dv, const PrefillParams& p, int stages, hipStream_t s);
+hipError_t prefill_bf16_c64(int dk, int dv, const PrefillParams& p, int stages, hipStream_t s);
+hipError_t prefill_f32_c16(int dk, int dv, const PrefillParams& p, int stages, hipStream_t s);
+hipError_t prefill_f32_c32(int dk, int dv, const PrefillParams& p, int stages, hipStream_t s);
+hipError_t prefill_f32_c64(int dk, int dv, const PrefillParams& p, int stages, hipStream_t s);
 
 hipError_t decode_bf16(int dk, int dv, const DecodeParams& p, hipStream_t s);
 hipError_t decode_f32(int dk, int dv, const DecodeParams& p, hipStream_t s);

@@ -414,15 +414,21 @@ __global__ __launch_bounds__(kThreads) void inter_chunk_kernel(PrefillParams p) 
     }
 }
 
+// stage bit 1: intra-chunk kernel; bit 2: inter-chunk kernel.
 template <typename E, int DK, int DV, int C>
-inline hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-    dim3 g1(p.N, p.Hv, p.B);
-    intra_chunk_kernel<E, DK, DV, C><<<g1, kThreads, 0, stream>>>(p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    dim3 g2(p.B * p.Hv * (DV / 16));
-    inter_chunk_kernel<E, DK, DV, C, sizeof(E) == 2><<<g2, kThreads, 0, stream>>>(p);
-    return hipGetLastError();
+inline hipError_t launch_prefill(const PrefillParams& p, int stages, hipStream_t stream) {
+    if (stages & 1) {
+        dim3 g1(p.N, p.Hv, p.B);
+        intra_chunk_kernel<E, DK, DV, C><<<g1, kThreads, 0, stream>>>(p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (stages & 2) {
+        dim3 g2(p.B * p.Hv * (DV / 16));
+        inter_chunk_kernel<E, DK, DV, C, sizeof(E) == 2><<<g2, kThreads, 0, stream>>>(p);
+        return hipGetLastError();
+    }
+    return hipSuccess;
 }
 
 }  // namespace gdn

@@ -17,12 +17,13 @@
 namespace gdn {
 
 template <int DK, int DV>
-static hipError_t run(const PrefillParams& p, hipStream_t s) {
-    return launch_prefill<GDN_E, DK, DV, GDN_CHUNK>(p, s);
+static hipError_t run(const PrefillParams& p, int stages, hipStream_t s) {
+    return launch_prefill<GDN_E, DK, DV, GDN_CHUNK>(p, stages, s);
 }
 
-hipError_t GDN_FN(GDN_TAG, GDN_CHUNK)(int dk, int dv, const PrefillParams& p, hipStream_t s) {
-    GDN_SWITCH_DIMS(dk, dv, run, p, s)
+hipError_t GDN_FN(GDN_TAG, GDN_CHUNK)(int dk, int dv, const PrefillParams& p, int stages,
+                                     hipStream_t s) {
+    GDN_SWITCH_DIMS(dk, dv, run, p, stages, s)
 }
 
 }  // namespace gdn

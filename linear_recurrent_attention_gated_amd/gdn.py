@@ -18,8 +18,8 @@ GDN_BF16 = 0
 GDN_F32 = 1
 _STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
            4: "GDN_ERR_ALIGN", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP"}
-EXPORTS = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode_step", "gdn_status_string",
-           "gdn_abi_version")
+EXPORTS = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_prepare", "gdn_prefill_scan",
+           "gdn_decode_step", "gdn_status_string", "gdn_abi_version")
 
 
 class GdnError(RuntimeError):
@@ -42,8 +42,9 @@ def lib():
         P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
         L.gdn_prefill_workspace_bytes.argtypes = [I] * 8
         L.gdn_prefill_workspace_bytes.restype = Z
-        L.gdn_prefill.argtypes = [P] * 8 + [I] * 8 + [P, Z, P]
-        L.gdn_prefill.restype = I
+        for fn in ("gdn_prefill", "gdn_prefill_prepare", "gdn_prefill_scan"):
+            getattr(L, fn).argtypes = [P] * 8 + [I] * 8 + [P, Z, P]
+            getattr(L, fn).restype = I
         L.gdn_decode_step.argtypes = [P] * 8 + [I] * 6 + [P]
         L.gdn_decode_step.restype = I
         L.gdn_status_string.argtypes = [I]
@@ -103,6 +104,23 @@ def gdn_prefill(q, k, v, g, beta, state_in, o, state_out, chunk, workspace, stre
     """Calls gdn_prefill.  q, k [B,T,Hk,dk]; v, o [B,T,Hv,dv] (bf16 or fp32); g, beta
     [B,T,Hv] fp32; state_in (or None) / state_out [B,Hv,dv,dk] fp32; workspace: a
     device tensor of at least gdn_prefill_workspace_bytes bytes (or None when T == 0)."""
+    _prefill_call("gdn_prefill", q, k, v, g, beta, state_in, o, state_out, chunk, workspace,
+                  stream)
+
+
+def gdn_prefill_prepare(q, k, v, g, beta, state_in, o, state_out, chunk, workspace, stream=None):
+    """Calls gdn_prefill_prepare (the state-independent stage); arguments as gdn_prefill."""
+    _prefill_call("gdn_prefill_prepare", q, k, v, g, beta, state_in, o, state_out, chunk,
+                  workspace, stream)
+
+
+def gdn_prefill_scan(q, k, v, g, beta, state_in, o, state_out, chunk, workspace, stream=None):
+    """Calls gdn_prefill_scan (the chunk-to-chunk stage); arguments as gdn_prefill."""
+    _prefill_call("gdn_prefill_scan", q, k, v, g, beta, state_in, o, state_out, chunk, workspace,
+                  stream)
+
+
+def _prefill_call(fn, q, k, v, g, beta, state_in, o, state_out, chunk, workspace, stream):
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
     dt = _dt(q)
@@ -117,11 +135,11 @@ def gdn_prefill(q, k, v, g, beta, state_in, o, state_out, chunk, workspace, stre
             (state_in is not None and tuple(state_in.shape) != (B, Hv, dv, dk)):
         raise ValueError("inconsistent shapes")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib().gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
-                           _ptr(o), _ptr(state_out), B, T, Hk, Hv, dk, dv, int(chunk), dt,
-                           _ptr(workspace), ws_bytes, _stream(stream))
+    rc = getattr(lib(), fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+                            _ptr(o), _ptr(state_out), B, T, Hk, Hv, dk, dv, int(chunk), dt,
+                            _ptr(workspace), ws_bytes, _stream(stream))
     if rc != 0:
-        raise GdnError("gdn_prefill", rc)
+        raise GdnError(fn, rc)
 
 
 def gdn_decode_step(q, k, v, g, beta, state_in, state_out, o, stream=None):

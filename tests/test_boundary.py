@@ -53,7 +53,7 @@ BASE = 1 << 40
 MB = 1 << 20
 
 
-def _prefill(**kw):
+def _prefill(fn="gdn_prefill", **kw):
     a = dict(q=BASE, k=BASE + 10 * MB, v=BASE + 20 * MB, g=BASE + 40 * MB, beta=BASE + 41 * MB,
              state_in=BASE + 50 * MB, o=BASE + 60 * MB, state_out=BASE + 80 * MB, B=1, T=64, Hk=2,
              Hv=4, dk=32, dv=32, chunk=16, dtype=0, ws=BASE + 100 * MB, ws_bytes=0, stream=None)
@@ -61,7 +61,7 @@ def _prefill(**kw):
     if "ws_bytes" not in kw:
         a["ws_bytes"] = gdn.gdn_prefill_workspace_bytes(a["B"], a["T"], a["Hk"], a["Hv"], a["dk"],
                                                         a["dv"], a["chunk"], a["dtype"])
-    return gdn.lib().gdn_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state_in"], a["o"],
+    return getattr(gdn.lib(), fn)(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state_in"], a["o"],
                                  a["state_out"], a["B"], a["T"], a["Hk"], a["Hv"], a["dk"], a["dv"],
                                  a["chunk"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
 
@@ -91,9 +91,10 @@ PREFILL_ERRORS = [
 ]
 
 
+@pytest.mark.parametrize("fn", ["gdn_prefill", "gdn_prefill_prepare", "gdn_prefill_scan"])
 @pytest.mark.parametrize("kw,code", PREFILL_ERRORS)
-def test_prefill_rejects(kw, code):
-    assert _prefill(**kw) == code
+def test_prefill_rejects(kw, code, fn):
+    assert _prefill(fn=fn, **kw) == code
 
 
 DECODE_ERRORS = [

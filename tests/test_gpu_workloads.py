@@ -1,0 +1,199 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark
+times, plus the properties the pages state or the method implies.
+
+Full sizes: the 4096-token prefill (all heads against the oracle, bf16 and fp32),
+the 32768-token continuation from a nonzero state (sampled heads -- every head is
+an independent recurrence, so the oracle computes the sampled ones exactly), the
+131072-token long-memory prefill (sampled heads) and its prefix sweep, and one
+decode token through 30 layers (looped and batched).
+
+Properties: segmenting a prompt and carrying the state gives the same output
+("Optimizing on-device inference for Apple Silicon", section "Bound temporary
+memory with prompt chunking"); key heads shared 2:1 give the same bytes as the
+duplicated heads (section "Pack query heads to reuse KV rows" makes the same
+point for attention); chunk size does not change the result; a one-token prefill
+equals a decode step; repeated runs are bitwise identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+from linear_recurrent_attention_gated_amd import gdn
+from linear_recurrent_attention_gated_amd.inputs import (CONTINUATION_32K, LONG_128K, PREFILL_4K,
+                                                         DECODE_LAYERS, decode_inputs,
+                                                         make_inputs, workload_inputs)
+from tests.gpu_util import TOL_O, TOL_S, nrel, np32, oracle_prefill, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = 16
+# value heads sampled for the long workloads: both heads of one key head, and heads spread
+# over the other key heads
+SAMPLED = [0, 1, 13, 22, 31]
+
+
+def gpu_prefill(d, chunk, state=None, dtype_ws=None):
+    dd = to_dev(d)
+    st = None if state is None else torch.as_tensor(np.asarray(state, np.float32)).cuda()
+    o, s = gdn.prefill(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], st, chunk=chunk)
+    torch.cuda.synchronize()
+    return o, s
+
+
+@pytest.fixture(scope="module")
+def c2_bf16():
+    d = workload_inputs(PREFILL_4K, torch.bfloat16)
+    o_ref, s_ref = oracle_prefill(d, nthreads=NTHREADS)
+    return d, o_ref, s_ref
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_prefill_4k_all_heads(dt, c2_bf16):
+    w = PREFILL_4K
+    if dt == "bf16":
+        d, o_ref, s_ref = c2_bf16
+    else:
+        d = workload_inputs(w, torch.float32)
+        o_ref, s_ref = oracle_prefill(d, nthreads=NTHREADS)
+    say("prefill 4k", dt)
+    o, s = gpu_prefill(d, w.chunk)
+    eo, es = nrel(np32(o), o_ref), nrel(s.cpu().numpy(), s_ref)
+    say("prefill 4k errors", dt, eo, es)
+    assert eo < TOL_O and es < TOL_S
+
+
+def test_continuation_32k_from_nonzero_state(c2_bf16):
+    w = CONTINUATION_32K
+    d0, _, s_c2 = c2_bf16
+    start = s_c2.astype(np.float32)          # the oracle's final state of the 4096-token prefill
+    d = workload_inputs(w, torch.bfloat16)
+    pairs = [(0, h) for h in SAMPLED]
+    say("continuation 32k")
+    o, s = gpu_prefill(d, w.chunk, start)
+    o_ref, s_ref = oracle_prefill(d, start.astype(np.float64), pairs=pairs, nthreads=NTHREADS)
+    o_g, s_g = np32(o), s.cpu().numpy()
+    for i, h in enumerate(SAMPLED):
+        eo, es = nrel(o_g[0, :, h], o_ref[i]), nrel(s_g[0, h], s_ref[i])
+        say("continuation head", h, eo, es)
+        assert eo < TOL_O and es < TOL_S
+    # chained on the GPU: its own 4096-token state carried into the continuation
+    _, s_gpu_c2 = gpu_prefill(d0, PREFILL_4K.chunk)
+    o2, s2 = gpu_prefill(d, w.chunk, s_gpu_c2.cpu().numpy())
+    o2g, s2g = np32(o2), s2.cpu().numpy()
+    for i, h in enumerate(SAMPLED):
+        assert nrel(o2g[0, :, h], o_ref[i]) < TOL_O and nrel(s2g[0, h], s_ref[i]) < TOL_S
+
+
+@pytest.fixture(scope="module")
+def c4():
+    d = workload_inputs(LONG_128K, torch.bfloat16)
+    say("long 128k: GPU run")
+    o, s = gpu_prefill(d, LONG_128K.chunk)
+    return d, np32(o), s.cpu().numpy()
+
+
+def test_long_128k_sampled_heads(c4):
+    d, o_g, s_g = c4
+    pairs = [(0, h) for h in SAMPLED[:3]]
+    o_ref, s_ref = oracle_prefill(d, pairs=pairs, nthreads=NTHREADS)
+    for i, (_, h) in enumerate(pairs):
+        eo, es = nrel(o_g[0, :, h], o_ref[i]), nrel(s_g[0, h], s_ref[i])
+        say("long head", h, eo, es)
+        assert eo < TOL_O and es < TOL_S
+        assert np.all(np.isfinite(o_g[0, :, h]))
+
+
+def test_long_sweep_prefixes(c4):
+    # the sweep T = 256, 512, ..., 65536 runs prefixes of the same draw; chunk-aligned prefixes
+    # go through identical chunk computations, so their outputs equal the full run's bitwise
+    d, o_full, _ = c4
+    for T in [256 << i for i in range(9)]:
+        dp = {k: (None if v is None else v[:, :T].contiguous()) for k, v in d.items()}
+        say("sweep prefix", T)
+        o, _ = gpu_prefill(dp, LONG_128K.chunk)
+        assert np.array_equal(np32(o), o_full[:, :T]), T
+
+
+def test_decode_30_layers_looped_and_batched():
+    layers = [decode_inputs(l) for l in range(DECODE_LAYERS)]
+    cat = {k: torch.cat([L[k] for L in layers]).cuda() for k in layers[0]}
+    st_loop = cat["state"].clone()
+    st_b = cat["state"].clone()
+    o_loop = torch.empty((DECODE_LAYERS, 32, 128), dtype=torch.bfloat16, device="cuda")
+    o_b = torch.empty_like(o_loop)
+    say("decode 30 layers")
+    for l in range(DECODE_LAYERS):
+        sl = slice(l, l + 1)
+        gdn.gdn_decode_step(cat["q"][sl], cat["k"][sl], cat["v"][sl], cat["g"][sl],
+                            cat["beta"][sl], st_loop[sl], st_loop[sl], o_loop[sl])
+    gdn.gdn_decode_step(cat["q"], cat["k"], cat["v"], cat["g"], cat["beta"], st_b, st_b, o_b)
+    torch.cuda.synchronize()
+    assert torch.equal(st_loop, st_b) and torch.equal(o_loop, o_b)
+    f = lambda t: t.float().numpy()  # noqa: E731
+    from oracle import gdn_oracle as orc
+    o_ref, s_ref = orc.decode_step(f(cat["q"].cpu()), f(cat["k"].cpu()), f(cat["v"].cpu()),
+                                   f(cat["g"].cpu()), f(cat["beta"].cpu()),
+                                   cat["state"].cpu().numpy().astype(np.float64))
+    for l in range(DECODE_LAYERS):
+        assert nrel(np32(o_loop[l]), o_ref[l]) < TOL_O
+        assert nrel(st_loop[l].cpu().numpy(), s_ref[l]) < 1e-6
+
+
+def test_split_invariance_state_carry():
+    d = make_inputs(1, 1000, 2, 4, 128, 128, seed=21, state_std=0.2)
+    o_full, s_full = gpu_prefill(d, 64, d["state"])
+    for T1 in (1, 64, 333):
+        a = {k: (v if k == "state" else v[:, :T1].contiguous()) for k, v in d.items()}
+        b = {k: (v if k == "state" else v[:, T1:].contiguous()) for k, v in d.items()}
+        say("split", T1)
+        oa, sa = gpu_prefill(a, 64, d["state"])
+        ob, sb = gpu_prefill(b, 64, sa.cpu().numpy())
+        o_cat = torch.cat([oa, ob], dim=1)
+        assert nrel(np32(o_cat), np32(o_full)) < 1e-2 and nrel(sb.cpu().numpy(), s_full.cpu().numpy()) < 5e-3
+        if T1 == 64:   # a chunk-aligned split runs the very same chunk computations
+            assert torch.equal(o_cat, o_full) and torch.equal(sb, s_full)
+
+
+def test_chunk_size_invariance():
+    d = make_inputs(1, 300, 2, 4, 64, 128, seed=22, state_std=0.2)
+    ref_o, ref_s = oracle_prefill(d, d["state"])
+    outs = {}
+    for C in (16, 32, 64):
+        say("chunk", C)
+        o, s = gpu_prefill(d, C, d["state"])
+        outs[C] = (np32(o), s.cpu().numpy())
+        assert nrel(outs[C][0], ref_o) < TOL_O and nrel(outs[C][1], ref_s) < TOL_S
+    assert nrel(outs[16][0], outs[64][0]) < 2e-2
+
+
+def test_single_token_prefill_equals_decode():
+    d = make_inputs(2, 1, 16, 32, 128, 128, seed=23, state_std=0.1)
+    o_p, s_p = gpu_prefill(d, 64, d["state"])
+    dd = to_dev(d)
+    st = dd["state"].clone()
+    say("T=1 vs decode")
+    o_d = gdn.decode_step(dd["q"][:, 0].contiguous(), dd["k"][:, 0].contiguous(),
+                          dd["v"][:, 0].contiguous(), dd["g"][:, 0].contiguous(),
+                          dd["beta"][:, 0].contiguous(), st)
+    torch.cuda.synchronize()
+    assert nrel(np32(o_p[:, 0]), np32(o_d)) < 1e-2
+    assert nrel(s_p.cpu().numpy(), st.cpu().numpy()) < 5e-3
+
+
+def test_shared_key_heads_equal_duplicated_heads_bitwise():
+    d = make_inputs(1, 200, 16, 32, 128, 128, seed=24)
+    dup = dict(d)
+    dup["q"] = d["q"].repeat_interleave(2, dim=2).contiguous()
+    dup["k"] = d["k"].repeat_interleave(2, dim=2).contiguous()
+    say("shared vs duplicated heads")
+    o1, s1 = gpu_prefill(d, 64)
+    o2, s2 = gpu_prefill(dup, 64)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_bitwise_deterministic():
+    d = make_inputs(1, 777, 2, 4, 128, 128, seed=25, state_std=0.1)
+    say("determinism")
+    o1, s1 = gpu_prefill(d, 64, d["state"])
+    o2, s2 = gpu_prefill(d, 64, d["state"])
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
