@@ -32,12 +32,15 @@ struct Layout {
 Layout layout(int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype dt) {
     const size_t es = elem_size(dt);
     const size_t N = ((size_t)T + chunk - 1) / chunk, Tp = N * (size_t)chunk;
+    // token-side k-blocks of the MFMA fragments are padded to 32 (bf16) / 4 (fp32) tokens
+    const size_t kb = dt == GDN_BF16 ? 32 : 4;
+    const size_t cp = ((size_t)chunk + kb - 1) / kb * kb;
     Layout L;
     size_t off = 0;
     L.W = off;   off = round_up(off + (size_t)B * Hv * Tp * dk * es, 256);
     L.Ut = off;  off = round_up(off + (size_t)B * Hv * Tp * dv * es, 256);
-    L.P = off;   off = round_up(off + (size_t)B * Hv * Tp * chunk * es, 256);
-    L.KT = off;  off = round_up(off + (size_t)B * Hk * Tp * dk * es, 256);
+    L.P = off;   off = round_up(off + (size_t)B * Hv * Tp * cp * es, 256);
+    L.KT = off;  off = round_up(off + (size_t)B * Hk * N * dk * cp * es, 256);
     L.gam = off; off = round_up(off + (size_t)B * Hv * Tp * sizeof(float), 256);
     L.total = off;
     return L;

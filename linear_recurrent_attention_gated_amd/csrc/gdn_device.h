@@ -25,12 +25,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN (quiet).
-__device__ __forceinline__ bf16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x0040u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 with the hardware conversion (v_cvt_pk_bf16_f32: round to nearest even,
+// NaN stays NaN).
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+    f32x2 x = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
@@ -50,9 +53,18 @@ template <> struct Elem<bf16_t> {
     }
     // fragment from 8 consecutive floats, rounded to bf16
     __device__ static __forceinline__ frag ld_f(const float* p) {
-        u16x8 u;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) u[e] = f2bf(p[e]);
+        uint4 u;
+        u.x = f2bf2(p[0], p[1]);
+        u.y = f2bf2(p[2], p[3]);
+        u.z = f2bf2(p[4], p[5]);
+        u.w = f2bf2(p[6], p[7]);
+        return __builtin_bit_cast(frag, u);
+    }
+    // the fragment, or zeros where `keep` is false (branch-free)
+    __device__ static __forceinline__ frag keep_if(frag a, bool keep) {
+        uint4 u = __builtin_bit_cast(uint4, a);
+        const uint32_t m = keep ? 0xffffffffu : 0u;
+        u.x &= m; u.y &= m; u.z &= m; u.w &= m;
         return __builtin_bit_cast(frag, u);
     }
     __device__ static __forceinline__ frag zero() {
@@ -73,11 +85,30 @@ template <> struct Elem<float> {
     __device__ static __forceinline__ frag ld(const float* p) { return *p; }
     __device__ static __forceinline__ frag ld_f(const float* p) { return *p; }
     __device__ static __forceinline__ frag zero() { return 0.0f; }
+    __device__ static __forceinline__ frag keep_if(frag a, bool keep) { return keep ? a : 0.0f; }
     __device__ static __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     }
 };
 
 __device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
+
+// Workgroup barrier for LDS traffic: wait until this wave's LDS reads and writes have
+// completed, then synchronise the waves.  Unlike __syncthreads() it does not wait for
+// outstanding global loads or stores, so prefetches and output stores stay in flight across
+// it.  The kernels here exchange data between waves only through LDS.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// fp32 16x16 output tile on the fp32 matrix cores: D = A(16 x K) B(K x 16) + D, with A and B
+// read from row-major fp32 LDS blocks (A rows lda apart, B rows ldb apart).  K % 4 == 0.
+__device__ __forceinline__ f32x4 mma_tile_f32(const float* A, int lda, const float* B, int ldb,
+                                              int K, f32x4 acc, int lane) {
+    const int r = lane & 15, kk = lane >> 4;
+    for (int k0 = 0; k0 < K; k0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * lda + k0 + kk], B[(k0 + kk) * ldb + r], acc, 0, 0, 0);
+    return acc;
+}
 
 }  // namespace gdn

@@ -176,8 +176,12 @@ def test_single_token_prefill_equals_decode():
                           dd["v"][:, 0].contiguous(), dd["g"][:, 0].contiguous(),
                           dd["beta"][:, 0].contiguous(), st)
     torch.cuda.synchronize()
-    assert nrel(np32(o_p[:, 0]), np32(o_d)) < 1e-2
-    assert nrel(s_p.cpu().numpy(), st.cpu().numpy()) < 5e-3
+    o_ref, s_ref = oracle_prefill(d, d["state"])
+    # both paths meet the tolerances against the oracle; the decode step (fp32 throughout)
+    # is far tighter on the state than the blockwise form (bf16 matrix-core operands)
+    assert nrel(np32(o_p), o_ref) < TOL_O and nrel(s_p.cpu().numpy(), s_ref) < TOL_S
+    assert nrel(np32(o_d), o_ref[:, 0]) < TOL_O and nrel(st.cpu().numpy(), s_ref) < 1e-6
+    assert nrel(np32(o_p[:, 0]), np32(o_d)) < TOL_O
 
 
 def test_shared_key_heads_equal_duplicated_heads_bitwise():
