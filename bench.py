@@ -56,18 +56,83 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+COPY_CALIBRATION_BYTES = 512 << 20
+
+
 def load_traffic():
-    """HBM bytes per launch measured with rocprofv3 counters (profiles/traffic.json), used only
-    while the kernel sources are unchanged since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/hbm_traffic.txt), used
+    only while the kernel sources are unchanged since the counters were taken."""
     try:
-        with open(path) as fh:
-            doc = json.load(fh)
+        with open(TRAFFIC_FILE) as fh:
+            doc = dict(l.split(":", 1) for l in fh.read().splitlines() if ":" in l and not l.startswith("#"))
     except (OSError, ValueError):
         return None
+    doc = {k.strip(): v.strip() for k, v in doc.items()}
     if doc.get("source_hash") != kernel_source_hash():
         return None
-    return doc
+    out = {}
+    for k, v in doc.items():
+        try:
+            out[k] = float(v)
+        except ValueError:
+            out[k] = v
+    return out
+
+
+def summarize_counters(fetch_dir, write_dir):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel from rocprofv3 CSV output,
+    scaled by what the same counters read for a plain copy of COPY_CALIBRATION_BYTES."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        sums = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as fh:
+                for row in csv.DictReader(fh):
+                    if row.get("Counter_Name") != counter:
+                        continue
+                    name = row.get("Kernel_Name", "")
+                    key = ("copy" if ("copy" in name.lower() or "elementwise" in name.lower())
+                           else "inter" if "inter_chunk_kernel" in name
+                           else "intra" if "intra_chunk_kernel" in name
+                           else "decode_L%d" % (int(float(row.get("Grid_Size", "0"))) // (256 * 256))
+                           if "decode_kernel" in name else None)
+                    if key is None:
+                        continue
+                    sums.setdefault(key, []).append(float(row["Counter_Value"]) * 1024.0)
+        # the calibration copy is the largest copy; small copies are runtime housekeeping
+        return {k: (max(v) if k == "copy" else sum(v) / len(v)) for k, v in sums.items()}
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    f_scale = fetch.get("copy", 0) / COPY_CALIBRATION_BYTES
+    w_scale = write.get("copy", 0) / COPY_CALIBRATION_BYTES
+    lines = ["# HBM bytes per dispatch (rocprofv3 FETCH_SIZE / WRITE_SIZE counters), made by:",
+             "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o fetch -- "
+             "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration" % fetch_dir,
+             "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o write -- "
+             "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration" % write_dir,
+             "#   python bench.py --summarize-counters %s %s" % (fetch_dir, write_dir),
+             "# Raw counter bytes are divided by the factor the same counter reads for a plain",
+             "# device-to-device copy of %d bytes (read and written once)." % COPY_CALIBRATION_BYTES,
+             "# decode_L<n>: one decode launch over n layers (B = n).",
+             "source_hash: %s" % kernel_source_hash(),
+             "fetch_scale: %.4f" % f_scale, "write_scale: %.4f" % w_scale]
+    for k in sorted(set(fetch) | set(write)):
+        if k == "copy":
+            continue
+        fb = fetch.get(k, 0.0) / f_scale if f_scale else 0.0
+        wb = write.get(k, 0.0) / w_scale if w_scale else 0.0
+        lines += ["%s_fetch_bytes: %.0f" % (k, fb), "%s_write_bytes: %.0f" % (k, wb),
+                  "%s_bytes: %.0f" % (k, fb + wb)]
+    fb = fetch.get("intra", 0.0) / f_scale + fetch.get("inter", 0.0) / f_scale if f_scale else 0.0
+    wb = write.get("intra", 0.0) / w_scale + write.get("inter", 0.0) / w_scale if w_scale else 0.0
+    lines.append("prefill_bytes_per_launch: %.0f" % (fb + wb))
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def parse():
@@ -78,11 +143,20 @@ def parse():
     ap.add_argument("--sets", type=int, default=6, help="rotating input buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=None)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain device-to-device copy of known size (the reference "
+                         "point for the HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script "
+                         "with --copy-calibration into profiles/hbm_traffic.txt, then exit")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the gated-delta-rule core is built and measured "
               "on a single MI355X; runs on more than one GPU are not supported.", file=sys.stderr)
@@ -197,6 +271,13 @@ def main():
     tw_intra = np.array([e[0].elapsed_time(e[1]) for e in evw]) * 1e3
     tw_inter = np.array([e[1].elapsed_time(e[2]) for e in evw]) * 1e3
 
+    if args.copy_calibration:   # one plain copy of known size for the byte counters
+        src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     mean_pf = float(t_prefill.mean())
     value = T / (mean_pf * 1e-6)
     pf_bytes = T * PREFILL_BYTES_PER_TOKEN + STATE_BYTES        # zero start state: state_out only
@@ -256,7 +337,7 @@ def main():
             "roofline": {"kernel": "decode_kernel, one launch over the 30 layers (B=30)",
                          "bound": "hbm", "achieved": round(dec_gbs_b, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(dec_gbs_b / HBM_PEAK_GBS, 4),
-                         "traffic": traffic_doc.get("decode_b30_bytes_per_launch") if traffic_doc else None,
+                         "traffic": traffic_doc.get("decode_L%d_bytes" % LAYERS) if traffic_doc else None,
                          "algorithmic_bytes_per_launch": dec_bytes_b},
         },
     }
