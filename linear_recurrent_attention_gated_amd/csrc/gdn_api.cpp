@@ -41,7 +41,7 @@ Layout layout(int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype
     L.Ut = off;  off = round_up(off + (size_t)B * Hv * Tp * dv * es, 256);
     L.P = off;   off = round_up(off + (size_t)B * Hv * Tp * cp * es, 256);
     L.KT = off;  off = round_up(off + (size_t)B * Hk * N * dk * cp * es, 256);
-    L.gam = off; off = round_up(off + (size_t)B * Hv * Tp * sizeof(float), 256);
+    L.gam = off; off = round_up(off + (size_t)B * Hv * Tp * 2 * sizeof(float), 256);
     L.total = off;
     return L;
 }

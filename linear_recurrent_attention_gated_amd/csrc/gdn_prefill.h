@@ -37,7 +37,8 @@
 //   P   [B][Hv][N][C/16][NKC]   fragments   A operand of P U     (rows tokens, k = tokens)
 //   KT  [B][Hk][N][DK/16][NKC]  fragments   A operand of K^T U'  (rows dk,     k = tokens)
 //   Ut  [B][Hv][N][DV/16][C/16] accumulator tiles (lane: col l % 16, rows 4 (l/16) + [0,4))
-//   gam [B][Hv][N*C] fp32 within-chunk running log-gate (rows past the end repeat the last)
+//   gam [B][Hv][N][2][C] fp32 gate factors per chunk: exp(gamma_r), then exp(gamma_last - gamma_r)
+//       (rows past the end repeat the last row's gamma)
 // NKC = ceil(C / KB); k-values past the chunk are stored as zeros.
 #pragma once
 
@@ -60,7 +61,7 @@ struct PrefillParams {
     void* Ut;
     void* P;
     void* KT;
-    float* gam;
+    float* gam;   // gate factors (see the workspace layout)
     int B, T, Hk, Hv, N;  // N = number of chunks
 };
 
@@ -383,33 +384,59 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
                 store_frag(Wg + ((size_t)f * 64 + lane) * KPL, Os + (m * 16 + rl) * LDO + kb * KB + kq);
             }
         }
-        if (tid < C) p.gam[bh * ((size_t)N * C) + t0 + tid] = sm_gam[tid];
+        if (tid < C) {   // gate factors for the scan: exp(gamma_r), then exp(gamma_last - gamma_r)
+            float* gf = p.gam + (bh * N + c) * 2 * C;
+            gf[tid] = expf(sm_gam[tid]);
+            gf[C + tid] = expf(sm_gam[C - 1] - sm_gam[tid]);
+        }
         lds_barrier();   // staging, V buffers and gates are reused by the next value head
     }
 }
 
 // ------------------------------------------------------------------------------------
 // Kernel 2: chunks in order; fp32 state slice in accumulator registers.
+//
+// Eight waves per workgroup in two roles.  Chain waves 0..3 carry the recurrence:
+// U = Ut - W S^T for their 16-token tile, then S^T <- Gamma_n S^T + K^T (e * U) for their
+// state tiles.  Output waves 4..7 compute O = Gamma (Q S^T) + P U for their token tile one
+// barrier behind, from a double-buffered copy of the state, so the output products stay off
+// the chain.  Each role prefetches its own operands NB chunks ahead into registers.
 // SPLIT: feed the state to W S^T as a bf16 hi + lo pair (two MFMAs) so the delta U sees
 // the fp32 state to ~16 bits instead of 8.
 // ------------------------------------------------------------------------------------
+constexpr int kScanThreads = 512;
+// operand sets in flight per wave: chain waves are on the critical path and prefetch
+// deeper; fp32 operands take four times the registers of bf16 ones
+template <typename E> struct ScanDepth;
+template <> struct ScanDepth<bf16_t> { static constexpr int chain = 3, output = 2; };
+template <> struct ScanDepth<float> { static constexpr int chain = 2, output = 1; };
+
 template <typename E, int DK, int C, int TPW>
-struct ScanOperands {
+struct ChainOperands {
     using X = Elem<E>;
     typedef typename X::frag frag;
     static constexpr int NKD = DK / X::KB;
     static constexpr int NKC = (C + X::KB - 1) / X::KB;
     frag w[NKD];
-    frag q[NKD];
-    frag p[NKC];
     frag kt[TPW][NKC];
     E ut[4];
-    f32x4 gam;
-    float glast;
+    f32x4 e;      // exp(gamma_last - gamma_r) for this lane's four token rows
+    float gn;     // exp(gamma_last)
+};
+
+template <typename E, int DK, int C>
+struct OutputOperands {
+    using X = Elem<E>;
+    typedef typename X::frag frag;
+    static constexpr int NKD = DK / X::KB;
+    static constexpr int NKC = (C + X::KB - 1) / X::KB;
+    frag q[NKD];
+    frag p[NKC];
+    f32x4 gr;     // exp(gamma_r) for this lane's four token rows
 };
 
 template <typename E, int DK, int DV, int C, bool SPLIT>
-__global__ __launch_bounds__(kThreads) void inter_chunk_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams p) {
     using Sh = PrefillShape<E, DK, DV, C>;
     using X = Elem<E>;
     typedef typename X::frag frag;
@@ -421,12 +448,14 @@ __global__ __launch_bounds__(kThreads) void inter_chunk_kernel(PrefillParams p) 
     constexpr int CP = NKC * KB;
     constexpr int LDU = CP + EPV;
     constexpr int NSLICE = DV / 16;
-    typedef ScanOperands<E, DK, C, TPW> Ops;
+    constexpr int NBC = ScanDepth<E>::chain, NBO = ScanDepth<E>::output;
+    typedef ChainOperands<E, DK, C, TPW> COps;
+    typedef OutputOperands<E, DK, C> OOps;
 
-    __shared__ __align__(16) E Sb[16 * LDS_];
-    __shared__ __align__(16) E Sl[SPLIT ? 16 * LDS_ : EPV];
-    __shared__ __align__(16) E UT[16 * LDU];
-    __shared__ __align__(16) E UsT[16 * LDU];
+    __shared__ __align__(16) E Sb[2][16 * LDS_];              // state slice, hi part, 2 buffers
+    __shared__ __align__(16) E Sl[2][SPLIT ? 16 * LDS_ : EPV];  // lo part
+    __shared__ __align__(16) E UT[16 * LDU];                   // U^T        (for P U)
+    __shared__ __align__(16) E UsT[16 * LDU];                  // (e * U)^T  (for the update)
 
     // XCD-aware placement: consecutive workgroups go to different XCDs; place the slices of
     // one head on the same XCD so they share its L2 for the head's chunk operands.
@@ -442,174 +471,191 @@ __global__ __launch_bounds__(kThreads) void inter_chunk_kernel(PrefillParams p) 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int rl = lane & 15, kq = (lane >> 4) * KPL, rq = (lane >> 4) * 4;
-    // Every wave fetches a token tile (waves past the chunk's tiles fetch a duplicate they do
-    // not use) and clamps its state tiles, so every prefetch load is unconditional and the
-    // compiler can count outstanding loads exactly instead of draining them.
-    const bool has_tile = wave < NT;
-    const int m = wave % NT;
+    const bool chain = wave < 4;
+    const int w4 = wave & 3;
+    const bool has_tile = w4 < NT;
+    const int m = w4 % NT;           // token tile (duplicate for waves past the chunk's tiles)
+    const int Nf = T / C;            // full chunks; a partial last chunk takes the tail path
+    std::integral_constant<bool, false> full;
+    std::integral_constant<bool, true> tail;
 
-    const E* Wg = reinterpret_cast<const E*>(p.W) + (size_t)bh * N * Sh::W_PER_CHUNK;
-    const E* Pg = reinterpret_cast<const E*>(p.P) + (size_t)bh * N * Sh::P_PER_CHUNK;
-    const E* Ug = reinterpret_cast<const E*>(p.Ut) + (size_t)bh * N * Sh::UT_PER_CHUNK;
-    const E* KTg = reinterpret_cast<const E*>(p.KT) + ((size_t)b * Hk + hk) * N * Sh::KT_PER_CHUNK;
-    const float* gg = p.gam + (size_t)bh * N * C;
-    const E* qg = reinterpret_cast<const E*>(p.q) + (size_t)hk * DK;
-    E* og = reinterpret_cast<E*>(p.o) + (size_t)h * DV + i0;
+    const float* gates = p.gam + (size_t)bh * N * 2 * C;   // per chunk: exp(gamma) then exp(gl - gamma)
 
-    // zero the U buffers once (columns past the chunk are read as zero k-values)
-    for (int e = tid; e < 16 * LDU; e += kThreads) {
+    for (int e = tid; e < 16 * LDU; e += kScanThreads) {   // columns past the chunk read as zero
         UT[e] = X::from_f(0.f);
         UsT[e] = X::from_f(0.f);
     }
 
-    // operands in the order the step consumes them: gates, W and Q, Ut, K^T, P
-    auto fetch = [&](Ops& op, int c) {
-        const int t0 = c * C;
-        op.glast = gg[(size_t)t0 + C - 1];
-        op.gam = *reinterpret_cast<const f32x4*>(gg + (size_t)t0 + m * 16 + rq);
-        const E* wsrc = Wg + (size_t)c * Sh::W_PER_CHUNK + (size_t)m * NKD * Sh::FRAG + lane * KPL;
-        const int tq = t0 + m * 16 + rl;
-        const E* qsrc = qg + ((size_t)b * T + min(tq, T - 1)) * Hk * DK + kq;
-#pragma unroll
-        for (int kb = 0; kb < NKD; ++kb) {
-            op.w[kb] = X::ld(wsrc + kb * Sh::FRAG);
-            op.q[kb] = X::ld(qsrc + kb * KB);   // rows past T are zeroed by the tail step
-        }
-        const E* usrc = Ug + (size_t)c * Sh::UT_PER_CHUNK + (((size_t)slice * NT + m) * 64 + lane) * 4;
-        if (sizeof(E) == 2) *reinterpret_cast<uint2*>(op.ut) = *reinterpret_cast<const uint2*>(usrc);
-        else *reinterpret_cast<uint4*>(op.ut) = *reinterpret_cast<const uint4*>(usrc);
-#pragma unroll
-        for (int tw = 0; tw < TPW; ++tw) {
-            const int dt = min(wave + 4 * tw, DT - 1);
-            const E* ksrc = KTg + (size_t)c * Sh::KT_PER_CHUNK + ((size_t)dt * NKC * 64 + lane) * KPL;
-#pragma unroll
-            for (int kb = 0; kb < NKC; ++kb) op.kt[tw][kb] = X::ld(ksrc + kb * Sh::FRAG);
-        }
-        const E* psrc = Pg + (size_t)c * Sh::P_PER_CHUNK + (size_t)m * NKC * Sh::FRAG + lane * KPL;
-#pragma unroll
-        for (int kb = 0; kb < NKC; ++kb) op.p[kb] = X::ld(psrc + kb * Sh::FRAG);
-    };
+    if (chain) {
+        const E* Wg = reinterpret_cast<const E*>(p.W) + (size_t)bh * N * Sh::W_PER_CHUNK;
+        const E* Ug = reinterpret_cast<const E*>(p.Ut) + (size_t)bh * N * Sh::UT_PER_CHUNK;
+        const E* KTg = reinterpret_cast<const E*>(p.KT) + ((size_t)b * Hk + hk) * N * Sh::KT_PER_CHUNK;
 
-    // state slice: S^T tiles (rows = dk index, cols = the 16 state rows of this slice)
-    f32x4 St[TPW];
-    const size_t sbase = ((size_t)bh * DV + i0 + rl) * DK;
+        auto fetch = [&](COps& op, int c) {
+            const float* gc = gates + (size_t)c * 2 * C;
+            op.gn = gc[C - 1];
+            op.e = *reinterpret_cast<const f32x4*>(gc + C + m * 16 + rq);
+            const E* wsrc = Wg + (size_t)c * Sh::W_PER_CHUNK + (size_t)m * NKD * Sh::FRAG + lane * KPL;
 #pragma unroll
-    for (int tw = 0; tw < TPW; ++tw) {
-        const int dt = wave + 4 * tw;
-        St[tw] = zero4();
-        if (dt < DT && p.state_in) {
-            const float4 s4 = *reinterpret_cast<const float4*>(p.state_in + sbase + dt * 16 + rq);
-            St[tw][0] = s4.x; St[tw][1] = s4.y; St[tw][2] = s4.z; St[tw][3] = s4.w;
-        }
-    }
-    // write the slice (rounded to the operand type; hi + lo when split) for the next chunk
-    auto publish = [&]() {
+            for (int kb = 0; kb < NKD; ++kb) op.w[kb] = X::ld(wsrc + kb * Sh::FRAG);
+            const E* usrc = Ug + (size_t)c * Sh::UT_PER_CHUNK + (((size_t)slice * NT + m) * 64 + lane) * 4;
+            if (sizeof(E) == 2) *reinterpret_cast<uint2*>(op.ut) = *reinterpret_cast<const uint2*>(usrc);
+            else *reinterpret_cast<uint4*>(op.ut) = *reinterpret_cast<const uint4*>(usrc);
+#pragma unroll
+            for (int tw = 0; tw < TPW; ++tw) {
+                const int dt = min(w4 + 4 * tw, DT - 1);
+                const E* ksrc = KTg + (size_t)c * Sh::KT_PER_CHUNK + ((size_t)dt * NKC * 64 + lane) * KPL;
+#pragma unroll
+                for (int kb = 0; kb < NKC; ++kb) op.kt[tw][kb] = X::ld(ksrc + kb * Sh::FRAG);
+            }
+        };
+
+        // state slice: S^T tiles (rows = dk index, cols = the 16 state rows of this slice)
+        f32x4 St[TPW];
+        const size_t sbase = ((size_t)bh * DV + i0 + rl) * DK;
 #pragma unroll
         for (int tw = 0; tw < TPW; ++tw) {
-            const int dt = wave + 4 * tw;
-            if (dt < DT) {
-                E hi[4], lo[4];
+            const int dt = w4 + 4 * tw;
+            St[tw] = zero4();
+            if (dt < DT && p.state_in) {
+                const float4 s4 = *reinterpret_cast<const float4*>(p.state_in + sbase + dt * 16 + rq);
+                St[tw][0] = s4.x; St[tw][1] = s4.y; St[tw][2] = s4.z; St[tw][3] = s4.w;
+            }
+        }
+        auto publish = [&](int buf) {
+#pragma unroll
+            for (int tw = 0; tw < TPW; ++tw) {
+                const int dt = w4 + 4 * tw;
+                if (dt < DT) {
+                    E hi[4], lo[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        hi[j] = X::from_f(St[tw][j]);
+                        lo[j] = X::from_f(St[tw][j] - X::to_f(hi[j]));
+                    }
+                    store4(&Sb[buf][rl * LDS_ + dt * 16 + rq], hi);
+                    if (SPLIT) store4(&Sl[buf][rl * LDS_ + dt * 16 + rq], lo);
+                }
+            }
+        };
+        auto step = [&](const COps& op, int c) {
+            const int cur = c & 1;
+            if (has_tile) {
+                const E* sr = &Sb[cur][rl * LDS_ + kq];
+                const E* sl = &Sl[cur][SPLIT ? rl * LDS_ + kq : 0];
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kb = 0; kb < NKD; ++kb) {
+                    acc = X::mma(op.w[kb], X::ld(sr + kb * KB), acc);
+                    if (SPLIT) acc = X::mma(op.w[kb], X::ld(sl + kb * KB), acc);
+                }
+                E u[4], us[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    hi[j] = X::from_f(St[tw][j]);
-                    lo[j] = X::from_f(St[tw][j] - X::to_f(hi[j]));
+                    const float uj = X::to_f(op.ut[j]) - acc[j];
+                    u[j] = X::from_f(uj);
+                    us[j] = X::from_f(uj * op.e[j]);
                 }
-                store4(Sb + rl * LDS_ + dt * 16 + rq, hi);
-                if (SPLIT) store4(Sl + rl * LDS_ + dt * 16 + rq, lo);
+                store4(UT + rl * LDU + m * 16 + rq, u);
+                store4(UsT + rl * LDU + m * 16 + rq, us);
             }
-        }
-    };
+            lds_barrier();   // (B1) U complete; chunk c's slice was read from buffer cur
+#pragma unroll
+            for (int tw = 0; tw < TPW; ++tw) {
+                const int dt = w4 + 4 * tw;
+                if (dt < DT) {
+                    f32x4 acc = St[tw] * op.gn;
+#pragma unroll
+                    for (int kb = 0; kb < NKC; ++kb)
+                        acc = X::mma(op.kt[tw][kb], X::ld(UsT + rl * LDU + kb * KB + kq), acc);
+                    St[tw] = acc;
+                }
+            }
+            publish(cur ^ 1);
+            lds_barrier();   // (B2) next slice published; output waves are done with U
+        };
 
-    // one chunk; TAIL: the final, partial chunk (output rows past T are not stored)
-    auto step = [&](const Ops& op, int c, auto tail) {
-        constexpr bool TAIL = decltype(tail)::value;
-        const int t0 = c * C;
-        // (1) U = Ut - W S^T and Q S^T for this wave's token tile
-        f32x4 oq = zero4();
-        const float Gn = expf(op.glast);
-        if (has_tile) {
-            const E* sr = Sb + rl * LDS_ + kq;
-            const E* sl = Sl + rl * LDS_ + kq;
-            f32x4 acc = zero4(), accq = zero4();
-            const bool qok = !TAIL || (t0 + m * 16 + rl < T);
+        publish(0);
+        COps op[NBC];
 #pragma unroll
-            for (int kb = 0; kb < NKD; ++kb) {
-                const frag bs = X::ld(sr + kb * KB);
-                acc = X::mma(op.w[kb], bs, acc);
-                if (SPLIT) acc = X::mma(op.w[kb], X::ld(sl + kb * KB), acc);
-                accq = X::mma(TAIL ? X::keep_if(op.q[kb], qok) : op.q[kb], bs, accq);
-            }
-            E u[4], us[4];
+        for (int j = 0; j < NBC; ++j) fetch(op[j], min(j, N - 1));
+        lds_barrier();
+        int c = 0;
+        for (; c + NBC <= N; c += NBC) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float uj = X::to_f(op.ut[j]) - acc[j];
-                u[j] = X::from_f(uj);
-                us[j] = X::from_f(uj * expf(op.glast - op.gam[j]));
-                oq[j] = expf(op.gam[j]) * accq[j];
+            for (int j = 0; j < NBC; ++j) {
+                step(op[j], c + j);
+                fetch(op[j], min(c + j + NBC, N - 1));
             }
-            store4(UT + rl * LDU + m * 16 + rq, u);
-            store4(UsT + rl * LDU + m * 16 + rq, us);
         }
-        lds_barrier();   // U complete; every wave has finished reading Sb
-        // (2) S^T <- Gamma_{n-1} S^T + K^T (exp(gamma_{n-1} - gamma) U), then republish
+#pragma unroll
+        for (int j = 0; j < NBC; ++j)
+            if (c + j < N) step(op[j], c + j);
+
 #pragma unroll
         for (int tw = 0; tw < TPW; ++tw) {
-            const int dt = wave + 4 * tw;
+            const int dt = w4 + 4 * tw;
             if (dt < DT) {
-                f32x4 acc = St[tw] * Gn;
-#pragma unroll
-                for (int kb = 0; kb < NKC; ++kb)
-                    acc = X::mma(op.kt[tw][kb], X::ld(UsT + rl * LDU + kb * KB + kq), acc);
-                St[tw] = acc;
+                float4 s4;
+                s4.x = St[tw][0]; s4.y = St[tw][1]; s4.z = St[tw][2]; s4.w = St[tw][3];
+                *reinterpret_cast<float4*>(p.state_out + sbase + dt * 16 + rq) = s4;
             }
         }
-        publish();
-        // (3) O = Gamma Q S^T + P U
-        if (has_tile) {
-            f32x4 acc = oq;
+    } else {
+        const E* Pg = reinterpret_cast<const E*>(p.P) + (size_t)bh * N * Sh::P_PER_CHUNK;
+        const E* qg = reinterpret_cast<const E*>(p.q) + (size_t)hk * DK;
+        E* og = reinterpret_cast<E*>(p.o) + (size_t)h * DV + i0;
+
+        auto fetch = [&](OOps& op, int c) {
+            const int t0 = c * C;
+            op.gr = *reinterpret_cast<const f32x4*>(gates + (size_t)c * 2 * C + m * 16 + rq);
+            const int tq = t0 + m * 16 + rl;
+            const E* qsrc = qg + ((size_t)b * T + min(tq, T - 1)) * Hk * DK + kq;
 #pragma unroll
-            for (int kb = 0; kb < NKC; ++kb) acc = X::mma(op.p[kb], X::ld(UT + rl * LDU + kb * KB + kq), acc);
+            for (int kb = 0; kb < NKD; ++kb) op.q[kb] = X::ld(qsrc + kb * KB);   // rows past T: zeroed in the tail
+            const E* psrc = Pg + (size_t)c * Sh::P_PER_CHUNK + (size_t)m * NKC * Sh::FRAG + lane * KPL;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = t0 + m * 16 + rq + j;
-                if (!TAIL || t < T) og[((size_t)b * T + t) * Hv * DV + rl] = X::from_f(acc[j]);
+            for (int kb = 0; kb < NKC; ++kb) op.p[kb] = X::ld(psrc + kb * Sh::FRAG);
+        };
+        auto step = [&](const OOps& op, int c, auto tailtag) {
+            constexpr bool TAIL = decltype(tailtag)::value;
+            const int t0 = c * C;
+            lds_barrier();   // (B1) U of chunk c is in LDS; buffer (c & 1) holds chunk c's slice
+            if (has_tile) {
+                const E* sr = &Sb[c & 1][rl * LDS_ + kq];
+                const bool qok = !TAIL || (t0 + m * 16 + rl < T);
+                f32x4 accq = zero4();
+#pragma unroll
+                for (int kb = 0; kb < NKD; ++kb)
+                    accq = X::mma(TAIL ? X::keep_if(op.q[kb], qok) : op.q[kb], X::ld(sr + kb * KB), accq);
+                f32x4 acc = accq * op.gr;
+#pragma unroll
+                for (int kb = 0; kb < NKC; ++kb) acc = X::mma(op.p[kb], X::ld(UT + rl * LDU + kb * KB + kq), acc);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int t = t0 + m * 16 + rq + j;
+                    if (!TAIL || t < T) og[((size_t)b * T + t) * Hv * DV + rl] = X::from_f(acc[j]);
+                }
+            }
+            lds_barrier();   // (B2)
+        };
+
+        OOps op[NBO];
+#pragma unroll
+        for (int j = 0; j < NBO; ++j) fetch(op[j], min(j, N - 1));
+        lds_barrier();
+        int c = 0;
+        for (; c + NBO <= Nf; c += NBO) {
+#pragma unroll
+            for (int j = 0; j < NBO; ++j) {
+                step(op[j], c + j, full);
+                fetch(op[j], min(c + j + NBO, N - 1));
             }
         }
-        lds_barrier();   // new slice visible; U buffers free
-    };
-
-    // Two operand sets alternate: while one chunk is processed the next is in flight and the
-    // one after is being requested.  Prefetch indices are clamped (a trailing refetch of the
-    // last chunk is harmless) so the loop body issues the same loads on every path.
-    publish();
-    Ops opA, opB;
-    fetch(opA, 0);
-    fetch(opB, min(1, N - 1));
-    lds_barrier();
-    const int Nf = T / C;   // full chunks
-    std::integral_constant<bool, false> full;
-    std::integral_constant<bool, true> tail;
-    int c = 0;
-    for (; c + 1 < Nf; c += 2) {
-        step(opA, c, full);
-        fetch(opA, min(c + 2, N - 1));
-        step(opB, c + 1, full);
-        fetch(opB, min(c + 3, N - 1));
-    }
-    if (c < Nf) {
-        step(opA, c, full);
-        if (c + 1 < N) step(opB, c + 1, tail);
-    } else if (c < N) {
-        step(opA, c, tail);
-    }
-
 #pragma unroll
-    for (int tw = 0; tw < TPW; ++tw) {
-        const int dt = wave + 4 * tw;
-        if (dt < DT) {
-            float4 s4;
-            s4.x = St[tw][0]; s4.y = St[tw][1]; s4.z = St[tw][2]; s4.w = St[tw][3];
-            *reinterpret_cast<float4*>(p.state_out + sbase + dt * 16 + rq) = s4;
+        for (int j = 0; j < NBO; ++j) {
+            if (c + j < Nf) step(op[j], c + j, full);
+            else if (c + j < N) step(op[j], c + j, tail);
         }
     }
 }
@@ -625,7 +671,7 @@ inline hipError_t launch_prefill(const PrefillParams& p, int stages, hipStream_t
     }
     if (stages & 2) {
         dim3 g2(p.B * p.Hv * (DV / 16));
-        inter_chunk_kernel<E, DK, DV, C, sizeof(E) == 2><<<g2, kThreads, 0, stream>>>(p);
+        inter_chunk_kernel<E, DK, DV, C, sizeof(E) == 2><<<g2, kScanThreads, 0, stream>>>(p);
         return hipGetLastError();
     }
     return hipSuccess;
