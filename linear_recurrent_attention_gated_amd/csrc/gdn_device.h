@@ -10,8 +10,8 @@
 //   A (16 x K): row  l % 16, k = (l / 16) * KPL + [0, KPL)
 //   B (K x 16): col  l % 16, k = (l / 16) * KPL + [0, KPL)
 //   D (16 x 16): col l % 16, rows (l / 16) * 4 + [0, 4)
-// All operands are read from memory laid out contiguous along k, so a bf16 fragment is
-// one 16-byte load and an fp32 fragment one 4-byte load.
+// Operands read from memory laid out contiguous along k are one 16-byte load per bf16
+// fragment and one 4-byte load per fp32 fragment.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,17 +38,46 @@ __device__ __forceinline__ uint32_t f2bf2(float a, float b) {
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // Element-type traits: load/store of q, k, v, o and the bf16/fp32 MFMA tile op.
+
+// Operand fragments read straight from accumulator tiles use a permuted k order: for k-block
+// kb and lane group g (= lane / 16), fragment element e holds k = kperm(kb, g, e).  With it a
+// 16x16 accumulator tile (lane: column l % 16, rows 4 g + [0, 4)) supplies KPL k-values per lane
+// without any lane exchange: bf16 blocks of 32 take rows 4g..4g+3 of tiles 2kb and 2kb+1;
+// fp32 blocks of 4 take row 4g + (kb & 3) of tile kb / 4.  Since a contraction sums over k,
+// any order works as long as both operands use the same one.
 template <typename E> struct Elem;
 
 template <> struct Elem<bf16_t> {
     static constexpr int KB = 32;   // k per MFMA
     static constexpr int KPL = 8;   // k per lane
     typedef bf16x8 frag;
+    __device__ static __forceinline__ int kperm(int kb, int g, int e) {
+        return 32 * kb + 16 * (e >> 2) + 4 * g + (e & 3);
+    }
+    // offset of element 0 of the permuted fragment (kb, g) in a k-contiguous row
+    __device__ static __forceinline__ int poff(int kb, int g) { return 32 * kb + 4 * g; }
+    // permuted fragment k-block kb from two accumulator tiles: lo = k-tile 2 kb, hi = 2 kb + 1
+    __device__ static __forceinline__ frag pack(f32x4 lo, f32x4 hi) {
+        uint4 u;
+        u.x = f2bf2(lo[0], lo[1]);
+        u.y = f2bf2(lo[2], lo[3]);
+        u.z = f2bf2(hi[0], hi[1]);
+        u.w = f2bf2(hi[2], hi[3]);
+        return __builtin_bit_cast(frag, u);
+    }
     __device__ static __forceinline__ float to_f(bf16_t x) { return bf2f(x); }
     __device__ static __forceinline__ bf16_t from_f(float x) { return f2bf(x); }
     // fragment at p[0..7] (16-byte aligned)
     __device__ static __forceinline__ frag ld(const bf16_t* p) {
         u16x8 u = *reinterpret_cast<const u16x8*>(p);
+        return __builtin_bit_cast(frag, u);
+    }
+    // permuted-order fragment of k-block kb from a k-contiguous row: row[kb * 32 + 4 g + 0..3]
+    // and row[kb * 32 + 16 + 4 g + 0..3]   (p = row + kb * 32 + 4 g, 8-byte aligned)
+    __device__ static __forceinline__ frag ld_perm(const bf16_t* p) {
+        uint2 a = *reinterpret_cast<const uint2*>(p);
+        uint2 b = *reinterpret_cast<const uint2*>(p + 16);
+        uint4 u = {a.x, a.y, b.x, b.y};
         return __builtin_bit_cast(frag, u);
     }
     // fragment from 8 consecutive floats, rounded to bf16
@@ -79,10 +108,15 @@ template <> struct Elem<bf16_t> {
 template <> struct Elem<float> {
     static constexpr int KB = 4;
     static constexpr int KPL = 1;
+    __device__ static __forceinline__ int kperm(int kb, int g, int) {
+        return 16 * (kb >> 2) + 4 * g + (kb & 3);
+    }
+    __device__ static __forceinline__ int poff(int kb, int g) { return kperm(kb, g, 0); }
     typedef float frag;
     __device__ static __forceinline__ float to_f(float x) { return x; }
     __device__ static __forceinline__ float from_f(float x) { return x; }
     __device__ static __forceinline__ frag ld(const float* p) { return *p; }
+    __device__ static __forceinline__ frag ld_perm(const float* p) { return *p; }
     __device__ static __forceinline__ frag ld_f(const float* p) { return *p; }
     __device__ static __forceinline__ frag zero() { return 0.0f; }
     __device__ static __forceinline__ frag keep_if(frag a, bool keep) { return keep ? a : 0.0f; }

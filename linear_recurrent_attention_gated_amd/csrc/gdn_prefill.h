@@ -16,25 +16,29 @@
 //
 // Only exponentials of gamma_r - gamma_s with s <= r appear, so no factor can overflow.
 //
-// Kernel 1 (intra_chunk_kernel), one workgroup per (batch, key head, chunk), fully
-// parallel.  The two Gram blocks K K^T and K Q^T are formed once on MFMA and kept in
-// registers; then for each value head reading this key head: masks with that head's
-// gates, (I + A) inverted in fp32 (16x16 diagonal blocks by substitution, then block
-// back-substitution), W and Ut on MFMA.  Everything the scan needs goes to the workspace
-// already arranged as MFMA operand fragments (see "Workspace layout").
+// Kernel 1 (intra_chunk_kernel), one workgroup per (batch, value head, chunk), fully
+// parallel: Gram blocks K K^T and K Q^T on MFMA, masks with the head's gates, (I + A)
+// inverted in fp32 (16x16 diagonal blocks by substitution, then block doubling on the fp32
+// matrix cores), W and Ut on MFMA.  Everything the scan needs goes to the workspace already
+// arranged as MFMA operands (see "Workspace layout"), written straight from the
+// accumulators.
 //
 // Kernel 2 (inter_chunk_kernel), one workgroup per (batch, value head, 16 state rows):
 // rows of S evolve independently (each needs only its own entries of v), so a head's
 // state is split into 16-row slices that never talk to each other.  The fp32 slice lives
 // in MFMA accumulator registers for the whole scan and is written back once at the end
 // ("Keep the recurrent state on chip": load the state once, carry it through the scan,
-// write it after).  Each chunk's operands are fetched two chunks ahead into registers, so
+// write it after).  Each chunk's operands are fetched chunks ahead into registers, so
 // the chunk-to-chunk chain waits only on LDS exchanges and matrix-core latency.
 //
-// Workspace layout (E = element type; every fragment is 64 lanes x KPL elements, lane l
-// holding row l % 16 and k-values (l / 16) * KPL + [0, KPL) of a 16 x KB tile):
-//   W   [B][Hv][N][C/16][DK/KB] fragments   A operand of W S^T   (rows tokens, k = dk)
-//   P   [B][Hv][N][C/16][NKC]   fragments   A operand of P U     (rows tokens, k = tokens)
+// Workspace layout (E = element type; a fragment is 64 lanes x KPL elements of a 16 x KB
+// operand tile, lane l holding row l % 16).  Fragments marked "permuted" hold, in lane group
+// g = l / 16, the k-values Elem<E>::kperm(kb, g, 0..KPL-1) of k-block kb; the others hold
+// k = kb * KB + g * KPL + [0, KPL).  The permuted order is the one an accumulator tile
+// provides without lane exchanges (see gdn_device.h), and the scan reads the matching
+// operand in the same order.
+//   W   [B][Hv][N][C/16][DK/KB] fragments   A operand of W S^T   (rows tokens, k = dk; permuted)
+//   P   [B][Hv][N][C/16][NKC]   fragments   A operand of P U     (rows tokens, k = tokens; permuted)
 //   KT  [B][Hk][N][DK/16][NKC]  fragments   A operand of K^T U'  (rows dk,     k = tokens)
 //   Ut  [B][Hv][N][DV/16][C/16] accumulator tiles (lane: col l % 16, rows 4 (l/16) + [0,4))
 //   gam [B][Hv][N][2][C] fp32 gate factors per chunk: exp(gamma_r), then exp(gamma_last - gamma_r)
@@ -101,295 +105,386 @@ __device__ __forceinline__ void store4(E* dst, const E* v) {
 }
 
 // ------------------------------------------------------------------------------------
-// Kernel 1: per-chunk, state-independent blocks.
+// Kernel 1: per-chunk, state-independent blocks; one workgroup per (batch, value head,
+// chunk), four waves.
+//
+//   phase 0  all global loads issued up front: K and V rows into registers, each wave's
+//            Q row tile as MFMA fragments, g and beta
+//   phase 1  K rows and K^T, V^T (token-contiguous) into LDS; wave 0 scans the gates
+//   phase 2  wave 0: Gram tiles of the diagonal blocks and of the first off-diagonal
+//            level, masked into A; unit-lower-triangular 16x16 diagonal inverses by
+//            substitution; first doubling level -- all wave-local.
+//            waves 1..3: their P row tiles (K Q^T on MFMA, masked, stored as permuted
+//            fragments straight from the accumulators), the remaining Gram tiles of A, the
+//            K^T fragments, and zeros above the block diagonal.
+//   phase 3  second doubling level (64-token chunks)
+//   phase 4  W^T = K^T diag(beta Gamma) R^T and Ut = R diag(beta) V on MFMA, stored from the
+//            accumulators (W as permuted fragments, Ut as accumulator tiles)
+// A is overwritten in place by R = (I + A)^-1.
 // ------------------------------------------------------------------------------------
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// wave-local ordering point for LDS traffic exchanged between lanes of one wave
+__device__ __forceinline__ void wave_lds_sync() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 template <typename E, int DK, int DV, int C>
 __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) {
     using S = PrefillShape<E, DK, DV, C>;
     using X = Elem<E>;
+    typedef typename X::frag frag;
     constexpr int KB = S::KB, KPL = S::KPL, NT = S::NT, NKD = S::NKD, NKC = S::NKC;
     constexpr int EPV = 16 / (int)sizeof(E);   // elements per 16-byte vector
-    constexpr int LDK = DK + EPV;              // row pitch of K rows (elements)
-    constexpr int LDV = DV + EPV;              // row pitch of V rows
+    constexpr int LDK = DK + EPV;              // K rows
     constexpr int CP = NKC * KB;               // chunk width padded to whole k-blocks
-    constexpr int LDT = CP + EPV;              // row pitch of token-contiguous (transposed) tiles
-    constexpr int LDA = C + 1;                 // fp32 A
-    constexpr int LDR = CP + 4;                // fp32 R, 16-byte aligned rows
-    constexpr int LDO = cmax(DK, CP) + EPV;    // W staging rows
-    constexpr int LDP = CP + EPV;              // P staging rows (inside the R area)
-    constexpr int LDX = C / 2 + 1;             // temporary of the block doubling
-    // LDS regions, reused across phases:
-    //   Y: K rows -> V^T -> W staging        Z: K^T (whole kernel)
-    //   X: V rows -> A and R (P staged inside the R area before R is formed)
-    constexpr int RY = cmax(cmax(C * LDK, DV * LDT), C * LDO);
-    constexpr int RZ = DK * LDT;
-    constexpr int RX = cmax(C * LDA + C * LDR, (C * LDV * (int)sizeof(E) + 3) / 4);
-    constexpr int NG = NT * (NT + 1) / 2;      // lower-triangular 16x16 tiles (incl. diagonal)
-    constexpr int GPW = (2 * NG + 3) / 4;      // Gram tiles held per wave
-    static_assert(C * LDP * (int)sizeof(E) <= C * LDR * 4, "P staging must fit in the R area");
+    constexpr int LDT = CP + EPV;              // token-contiguous rows (K^T, V^T)
+    constexpr int LDR = CP + 4;                // fp32 A / R rows
+    constexpr int ND = DK / 16, NV = DV / 16;
+    static_assert(NT == 1 || NT == 2 || NT == 4, "chunk of 16, 32 or 64 tokens");
+    constexpr float LOG2E = 1.4426950408889634f;
 
-    __shared__ __align__(16) E sm_y[RY];
-    __shared__ __align__(16) E sm_z[RZ];
-    __shared__ __align__(16) float sm_x[RX];
-    __shared__ float sm_t[(C / 2 > 16 ? C / 2 : 16) * LDX];
-    __shared__ float sm_gam[C];
-    __shared__ float sm_beta[CP];
-    __shared__ float sm_bg[CP];   // beta * Gamma
+    __shared__ __align__(16) E Ks[C * LDK];
+    __shared__ __align__(16) E KsT[DK * LDT];
+    __shared__ __align__(16) E VsT[DV * LDT];
+    __shared__ __align__(16) float sR[C * LDR];   // A, then R in place
+    __shared__ __align__(16) float sg2[C];        // gamma * log2(e)
+    __shared__ __align__(16) float sbeta[CP];
+    __shared__ __align__(16) float sbg[CP];       // beta * Gamma
 
-    const int c = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int T = p.T, Hk = p.Hk, Hv = p.Hv, N = p.N;
-    const int grp = Hv / Hk;
+    const int grp = Hv / Hk, hk = h / grp;
     const int t0 = c * C;
     const int n = min(C, T - t0);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int rl = lane & 15, kq = (lane >> 4) * KPL, rq = (lane >> 4) * 4;
-
-    const E* kg = reinterpret_cast<const E*>(p.k) + ((size_t)b * T + t0) * Hk * DK + (size_t)hk * DK;
-    const E* qg = reinterpret_cast<const E*>(p.q) + ((size_t)b * T + t0) * Hk * DK + (size_t)hk * DK;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rl = lane & 15, g = lane >> 4, kq = g * KPL, rq = g * 4;
     const size_t rsk = (size_t)Hk * DK, rsv = (size_t)Hv * DV;
+    const size_t bh = (size_t)b * Hv + h;
 
-    E* Ks = sm_y;
-    E* KsT = sm_z;
-    E* VsT = sm_y;
-    E* Os = sm_y;
-    E* Vs = reinterpret_cast<E*>(sm_x);
-    float* sA = sm_x;
-    float* sR = sm_x + C * LDA;
-    E* Ps = reinterpret_cast<E*>(sR);
+    const E* kg = reinterpret_cast<const E*>(p.k) + ((size_t)b * T + t0) * rsk + (size_t)hk * DK;
+    const E* qg = reinterpret_cast<const E*>(p.q) + ((size_t)b * T + t0) * rsk + (size_t)hk * DK;
+    const E* vg = reinterpret_cast<const E*>(p.v) + ((size_t)b * T + t0) * rsv + (size_t)h * DV;
 
-    // -- K rows (rows >= n are zero) -----------------------------------------------------------
-    constexpr int VK = DK / EPV;
-    for (int idx = tid; idx < C * VK; idx += kThreads) {
-        const int r = idx / VK, cv = idx % VK;
-        uint4 a = {0u, 0u, 0u, 0u};
-        if (r < n) a = *reinterpret_cast<const uint4*>(kg + r * rsk + cv * EPV);
-        *reinterpret_cast<uint4*>(Ks + r * LDK + cv * EPV) = a;
+    // ---- phase 0: loads (rows past the chunk's end read row n - 1 and are zeroed later) ------
+    constexpr int VK = DK / EPV, VV = DV / EPV;
+    constexpr int PK = (C * VK + kThreads - 1) / kThreads, PV = (C * VV + kThreads - 1) / kThreads;
+    uint4 kr[PK], vr[PV];
+#pragma unroll
+    for (int i = 0; i < PK; ++i) {
+        const int idx = min(tid + i * kThreads, C * VK - 1), r = idx % C, cv = idx / C;
+        kr[i] = *reinterpret_cast<const uint4*>(kg + (size_t)min(r, n - 1) * rsk + cv * EPV);
     }
-    lds_barrier();
-
-    // -- K^T (token-contiguous, zero tokens up to CP); adjacent lanes read adjacent columns -----
-    for (int idx = tid; idx < DK * (CP / EPV); idx += kThreads) {
-        const int d = idx % DK, s0 = (idx / DK) * EPV;
-        uint4 raw;
-        E* tmp = reinterpret_cast<E*>(&raw);
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) tmp[e] = (s0 + e < C) ? Ks[(s0 + e) * LDK + d] : X::from_f(0.f);
-        *reinterpret_cast<uint4*>(KsT + d * LDT + s0) = raw;
+    for (int i = 0; i < PV; ++i) {
+        const int idx = min(tid + i * kThreads, C * VV - 1), r = idx % C, cv = idx / C;
+        vr[i] = *reinterpret_cast<const uint4*>(vg + (size_t)min(r, n - 1) * rsv + cv * EPV);
     }
-
-    // -- Gram tiles on MFMA, kept in registers across the value heads -------------------------
-    //   ti <  NG: K K^T, D[r][s]  (r in tile tm, s in tile tn)
-    //   ti >= NG: K Q^T, D[s][r]  (s in tile tn, r in tile tm), i.e. P^T before masking;
-    //             the Q rows come straight from global memory.
-    f32x4 G[GPW];
-#pragma unroll
-    for (int gi = 0; gi < GPW; ++gi) {
-        const int ti = wave + 4 * gi;
-        G[gi] = zero4();
-        if (ti < 2 * NG) {
-            const bool isq = ti >= NG;
-            int tm, tn;
-            lower_tile(isq ? ti - NG : ti, tm, tn);
-            const E* ar = Ks + ((isq ? tn : tm) * 16 + rl) * LDK + kq;
-            f32x4 acc = zero4();
-            if (!isq) {
-                const E* br = Ks + (tn * 16 + rl) * LDK + kq;
-#pragma unroll
-                for (int kb = 0; kb < NKD; ++kb) acc = X::mma(X::ld(ar + kb * KB), X::ld(br + kb * KB), acc);
-            } else {
-                const int rq_row = tm * 16 + rl;
-                const E* br = qg + (size_t)rq_row * rsk + kq;
-#pragma unroll
-                for (int kb = 0; kb < NKD; ++kb) {
-                    const typename X::frag bq = (rq_row < n) ? X::ld(br + kb * KB) : X::zero();
-                    acc = X::mma(X::ld(ar + kb * KB), bq, acc);
-                }
-            }
-            G[gi] = acc;
-        }
-    }
-    lds_barrier();   // K^T complete; K rows no longer needed
-
-    // -- K^T fragments for the scan (written once per key head) -------------------------------
+    // this wave's P row tile: wave 0 takes row 0, wave w >= 1 row NT - w (if >= 1)
+    const int pm = wave == 0 ? 0 : NT - wave;
+    const bool has_prow = wave == 0 || pm >= 1;
+    const int pm_ld = max(pm, 0);
+    frag qf[NKD];
     {
-        E* KTg = reinterpret_cast<E*>(p.KT) + (((size_t)b * Hk + hk) * N + c) * S::KT_PER_CHUNK;
-        for (int f = wave; f < (DK / 16) * NKC; f += kThreads / 64) {
-            const int dt = f / NKC, kb = f % NKC;
-            store_frag(KTg + ((size_t)f * 64 + lane) * KPL, KsT + (dt * 16 + rl) * LDT + kb * KB + kq);
+        const int row = pm_ld * 16 + rl;
+        const E* src = qg + (size_t)min(row, n - 1) * rsk + kq;
+#pragma unroll
+        for (int kb = 0; kb < NKD; ++kb) qf[kb] = X::ld(src + kb * KB);
+    }
+    const size_t gidx = ((size_t)b * T + t0 + min(lane, n - 1)) * Hv + h;
+    const float graw = p.g[gidx], braw = p.beta[gidx];
+
+    // ---- phase 1: K rows, K^T and V^T into LDS; gates -----------------------------------------
+#pragma unroll
+    for (int i = 0; i < PK; ++i) {
+        const int idx = tid + i * kThreads;
+        if (idx < C * VK) {
+            const int r = idx % C, cv = idx / C;
+            const uint4 z = {0u, 0u, 0u, 0u};
+            const uint4 a = r < n ? kr[i] : z;
+            *reinterpret_cast<uint4*>(Ks + r * LDK + cv * EPV) = a;
+            const E* e = reinterpret_cast<const E*>(&a);
+#pragma unroll
+            for (int j = 0; j < EPV; ++j) KsT[(cv * EPV + j) * LDT + r] = e[j];
         }
     }
+#pragma unroll
+    for (int i = 0; i < PV; ++i) {
+        const int idx = tid + i * kThreads;
+        if (idx < C * VV) {
+            const int r = idx % C, cv = idx / C;
+            const uint4 z = {0u, 0u, 0u, 0u};
+            const uint4 a = r < n ? vr[i] : z;
+            const E* e = reinterpret_cast<const E*>(&a);
+#pragma unroll
+            for (int j = 0; j < EPV; ++j) VsT[(cv * EPV + j) * LDT + r] = e[j];
+        }
+    }
+    if (CP > C) {   // token columns past the chunk (16-token chunks in bf16)
+        for (int e = tid; e < (DK + DV) * (CP - C); e += kThreads) {
+            const int d = e / (CP - C), s = C + e % (CP - C);
+            if (d < DK) KsT[d * LDT + s] = X::from_f(0.f);
+            else VsT[(d - DK) * LDT + s] = X::from_f(0.f);
+        }
+    }
+    if (wave == 0) {
+        float x = lane < n ? graw : 0.f;   // running log-gate; constant past the end
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        const float bt = lane < n ? braw : 0.f;
+        const float x2 = x * LOG2E;
+        const float gl2 = __shfl(x2, C - 1, 64);
+        if (lane < C) sg2[lane] = x2;
+        if (lane < CP) {
+            sbeta[lane] = bt;
+            sbg[lane] = bt * exp2f(x2);
+        }
+        if (lane < C) {   // gate factors for the scan: exp(gamma_r), exp(gamma_last - gamma_r)
+            float* gf = p.gam + (bh * N + c) * 2 * C;
+            gf[lane] = exp2f(x2);
+            gf[C + lane] = exp2f(gl2 - x2);
+        }
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKD; ++kb) qf[kb] = X::keep_if(qf[kb], pm_ld * 16 + rl < n);
+    lds_barrier();   // (B1)
 
-    for (int hh = 0; hh < grp; ++hh) {
-        const int h = hk * grp + hh;
-        const size_t bh = (size_t)b * Hv + h;
-
-        // -- gates: running log-gate over the chunk, beta, beta * Gamma; V rows ----------------
-        if (wave == 0) {
-            const size_t gi = ((size_t)b * T + t0 + lane) * Hv + h;
-            float x = (lane < n) ? p.g[gi] : 0.f;
+    // Gram tile of K rows: D[r][s] = k_r . k_s  (r in tile tm, s in tile tn)
+    auto kk_tile = [&](int tm, int tn) {
+        const E* ar = Ks + (tm * 16 + rl) * LDK + kq;
+        const E* br = Ks + (tn * 16 + rl) * LDK + kq;
+        f32x4 acc = zero4();
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off, 64);
-                if (lane >= off) x += y;
-            }
-            const float bt = (lane < n) ? p.beta[gi] : 0.f;
-            if (lane < C) sm_gam[lane] = x;
-            if (lane < CP) {
-                sm_beta[lane] = bt;
-                sm_bg[lane] = bt * expf(x);
-            }
+        for (int kb = 0; kb < NKD; ++kb) acc = X::mma(X::ld(ar + kb * KB), X::ld(br + kb * KB), acc);
+        return acc;
+    };
+    // A[r][s] = beta_r exp(gamma_r - gamma_s) (k_r . k_s) for s < r, from a Gram tile
+    auto mask_a = [&](int tm, int tn, f32x4 G) {
+        const int s = tn * 16 + rl;
+        const float gs = sg2[s];
+        const float4 gr = *reinterpret_cast<const float4*>(sg2 + tm * 16 + rq);
+        const float4 br = *reinterpret_cast<const float4*>(sbeta + tm * 16 + rq);
+        const float grv[4] = {gr.x, gr.y, gr.z, gr.w}, brv[4] = {br.x, br.y, br.z, br.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = tm * 16 + rq + j;
+            sR[r * LDR + s] = (s < r) ? brv[j] * exp2f(grv[j] - gs) * G[j] : 0.f;
         }
-        const E* vg = reinterpret_cast<const E*>(p.v) + ((size_t)b * T + t0) * rsv + (size_t)h * DV;
-        constexpr int VV = DV / EPV;
-        for (int idx = tid; idx < C * VV; idx += kThreads) {
-            const int r = idx / VV, cv = idx % VV;
-            uint4 a = {0u, 0u, 0u, 0u};
-            if (r < n) a = *reinterpret_cast<const uint4*>(vg + r * rsv + cv * EPV);
-            *reinterpret_cast<uint4*>(Vs + r * LDV + cv * EPV) = a;
-        }
-        lds_barrier();
-        for (int idx = tid; idx < DV * (CP / EPV); idx += kThreads) {
-            const int d = idx % DV, s0 = (idx / DV) * EPV;
-            uint4 raw;
-            E* tmp = reinterpret_cast<E*>(&raw);
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) tmp[e] = (s0 + e < C) ? Vs[(s0 + e) * LDV + d] : X::from_f(0.f);
-            *reinterpret_cast<uint4*>(VsT + d * LDT + s0) = raw;
-        }
-        lds_barrier();   // V rows consumed: the X area now holds A and R
-
-        // -- masks: A (fp32) and P (staged as P[r][s] in the R area) ---------------------------
-#pragma unroll
-        for (int gi = 0; gi < GPW; ++gi) {
-            const int ti = wave + 4 * gi;
-            if (ti < 2 * NG) {
-                const bool isq = ti >= NG;
-                int tm, tn;
-                lower_tile(isq ? ti - NG : ti, tm, tn);
-                if (!isq) {
-                    const int s = tn * 16 + rl;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int r = tm * 16 + rq + j;
-                        sA[r * LDA + s] = (s < r) ? sm_beta[r] * expf(sm_gam[r] - sm_gam[s]) * G[gi][j] : 0.f;
-                    }
-                } else {
-                    const int r = tm * 16 + rl;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int s = tn * 16 + rq + j;
-                        const float val = (s <= r) ? expf(sm_gam[r] - sm_gam[s]) * G[gi][j] : 0.f;
-                        Ps[r * LDP + s] = X::from_f(val);
-                    }
-                }
-            }
-        }
-        for (int e = tid; e < C * CP; e += kThreads) {   // tiles above the diagonal are zero
-            const int r = e / CP, s = e % CP;
-            if ((s >> 4) > (r >> 4)) {
-                if (s < C) sA[r * LDA + s] = 0.f;
-                Ps[r * LDP + s] = X::from_f(0.f);
-            }
-        }
-        lds_barrier();
-        {
-            E* Pg = reinterpret_cast<E*>(p.P) + (bh * N + c) * S::P_PER_CHUNK;
-            for (int f = wave; f < NT * NKC; f += kThreads / 64) {
-                const int m = f / NKC, kb = f % NKC;
-                store_frag(Pg + ((size_t)f * 64 + lane) * KPL, Ps + (m * 16 + rl) * LDP + kb * KB + kq);
-            }
-        }
-        lds_barrier();   // P staging consumed: the R area is free
-
-        // -- R = (I + A)^-1: 16x16 diagonal blocks by substitution, then block doubling ------
-        if (tid < NT * 16) {
-            const int base = (tid >> 4) * 16, j = tid & 15;
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float s = (r == j) ? 1.f : 0.f;
-#pragma unroll
-                for (int m = 0; m < r; ++m) s -= sA[(base + r) * LDA + base + m] * x[m];
-                x[r] = s;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sR[(base + r) * LDR + base + j] = x[r];
-        }
-        for (int e = tid; e < C * CP; e += kThreads) {
-            const int r = e / CP, s = e % CP;
-            if ((s >> 4) > (r >> 4)) sR[r * LDR + s] = 0.f;
-        }
-        lds_barrier();
-        // [[R11, 0], [R21, R22]] with R21 = -R22 A21 R11, for block sizes 16, 32, ... < C
-        for (int bs = 16; bs < C; bs *= 2) {
-            const int npair = C / (2 * bs), tpb = bs / 16, tiles = npair * tpb * tpb;
-            for (int t = wave; t < tiles; t += kThreads / 64) {
-                const int pr = t / (tpb * tpb), ti = (t % (tpb * tpb)) / tpb, tj = t % tpb;
-                const int lo = pr * 2 * bs, hi = lo + bs;
-                const f32x4 acc = mma_tile_f32(sA + (hi + ti * 16) * LDA + lo, LDA,
-                                               sR + lo * LDR + lo + tj * 16, LDR, bs, zero4(), lane);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sm_t[(pr * bs + ti * 16 + rq + j) * LDX + tj * 16 + rl] = acc[j];
-            }
-            lds_barrier();
-            for (int t = wave; t < tiles; t += kThreads / 64) {
-                const int pr = t / (tpb * tpb), ti = (t % (tpb * tpb)) / tpb, tj = t % tpb;
-                const int lo = pr * 2 * bs, hi = lo + bs;
-                const f32x4 acc = mma_tile_f32(sR + (hi + ti * 16) * LDR + hi, LDR,
-                                               sm_t + (pr * bs) * LDX + tj * 16, LDX, bs, zero4(), lane);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sR[(hi + ti * 16 + rq + j) * LDR + lo + tj * 16 + rl] = -acc[j];
-            }
-            lds_barrier();
-        }
-
-        // -- Ut = R diag(beta) V as accumulator tiles, then W = R diag(beta Gamma) K staged ----
-        auto rtile = [&](int tm, const float* scale, const E* bsrc) {
-            const float* arow = sR + (tm * 16 + rl) * LDR + kq;
+    };
+    // P row tile m: P[r][s] = exp(gamma_r - gamma_s) (q_r . k_s), s <= r, stored as permuted
+    // A-operand fragments (rows r, k = s) built from tiles D[s][r] = K_t Q_m^T
+    auto p_row = [&](int m) {
+        E* Pg = reinterpret_cast<E*>(p.P) + (bh * N + c) * S::P_PER_CHUNK;
+        const int r = m * 16 + rl;
+        const float gr = sg2[r];
+        auto ptile = [&](int t) {
             f32x4 acc = zero4();
+            if (t <= m) {
+                const E* ar = Ks + (t * 16 + rl) * LDK + kq;
 #pragma unroll
-            for (int kb = 0; kb < NKC; ++kb) {
-                float av[KPL];
+                for (int kb = 0; kb < NKD; ++kb) acc = X::mma(X::ld(ar + kb * KB), qf[kb], acc);
+                const float4 gs = *reinterpret_cast<const float4*>(sg2 + t * 16 + rq);
+                const float gsv[4] = {gs.x, gs.y, gs.z, gs.w};
 #pragma unroll
-                for (int e = 0; e < KPL; ++e) av[e] = arow[kb * KB + e] * scale[kb * KB + kq + e];
-                acc = X::mma(X::ld_f(av), X::ld(bsrc + kb * KB), acc);
+                for (int j = 0; j < 4; ++j) {
+                    const int s = t * 16 + rq + j;
+                    acc[j] = (s <= r) ? exp2f(gr - gsv[j]) * acc[j] : 0.f;
+                }
             }
             return acc;
         };
-        {
-            E* Ug = reinterpret_cast<E*>(p.Ut) + (bh * N + c) * S::UT_PER_CHUNK;
-            for (int ti = wave; ti < NT * (DV / 16); ti += kThreads / 64) {
-                const int tm = ti / (DV / 16), tn = ti % (DV / 16);
-                const f32x4 acc = rtile(tm, sm_beta, VsT + (tn * 16 + rl) * LDT + kq);
-                E ov[4];
+        if constexpr (KPL == 8) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) ov[j] = X::from_f(acc[j]);
-                store4(Ug + (((size_t)tn * NT + tm) * 64 + lane) * 4, ov);
+            for (int kb = 0; kb < NKC; ++kb) {
+                const frag f = X::pack(ptile(2 * kb), 2 * kb + 1 < NT ? ptile(2 * kb + 1) : zero4());
+                *reinterpret_cast<frag*>(Pg + ((size_t)(m * NKC + kb) * 64 + lane) * KPL) = f;
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const f32x4 d = ptile(t);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Pg[(size_t)(m * NKC + 4 * t + j) * 64 + lane] = X::from_f(d[j]);
             }
         }
-        lds_barrier();   // V^T consumed: Y becomes the W staging area
-        for (int ti = wave; ti < NT * (DK / 16); ti += kThreads / 64) {
-            const int tm = ti / (DK / 16), tn = ti % (DK / 16);
-            const f32x4 acc = rtile(tm, sm_bg, KsT + (tn * 16 + rl) * LDT + kq);
+    };
+
+    // ---- phase 2 -------------------------------------------------------------------------------
+    if (wave == 0) {
+        f32x4 Gd[NT], G1[NT / 2 > 0 ? NT / 2 : 1];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) Os[(tm * 16 + rq + j) * LDO + tn * 16 + rl] = X::from_f(acc[j]);
+        for (int d = 0; d < NT; ++d) Gd[d] = kk_tile(d, d);
+#pragma unroll
+        for (int q = 0; q < NT / 2; ++q) G1[q] = kk_tile(2 * q + 1, 2 * q);
+        p_row(0);
+#pragma unroll
+        for (int d = 0; d < NT; ++d) mask_a(d, d, Gd[d]);
+#pragma unroll
+        for (int q = 0; q < NT / 2; ++q) mask_a(2 * q + 1, 2 * q, G1[q]);
+        wave_lds_sync();
+        // (I + A_dd)^-1 of each 16x16 diagonal block by forward substitution: lane (d, j)
+        // computes column j of block d
+        if (g < NT) {
+            float* Ab = sR + (g * 16) * LDR + g * 16;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float a[16];
+#pragma unroll
+                for (int m4 = 0; m4 < (r + 3) / 4; ++m4) {
+                    const float4 v = *reinterpret_cast<const float4*>(Ab + r * LDR + 4 * m4);
+                    a[4 * m4] = v.x; a[4 * m4 + 1] = v.y; a[4 * m4 + 2] = v.z; a[4 * m4 + 3] = v.w;
+                }
+                float s0 = (r == rl) ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+                for (int m = 0; m < r; ++m) {
+                    if (m & 1) s1 -= a[m] * x[m];
+                    else s0 -= a[m] * x[m];
+                }
+                x[r] = s0 + s1;
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Ab[r * LDR + rl] = x[r];
         }
-        lds_barrier();
-        {
-            E* Wg = reinterpret_cast<E*>(p.W) + (bh * N + c) * S::W_PER_CHUNK;
-            for (int f = wave; f < NT * NKD; f += kThreads / 64) {
-                const int m = f / NKD, kb = f % NKD;
-                store_frag(Wg + ((size_t)f * 64 + lane) * KPL, Os + (m * 16 + rl) * LDO + kb * KB + kq);
+        wave_lds_sync();
+        // first doubling level: R21 = -R22 (A21 R11) for the block pairs (2q, 2q + 1)
+#pragma unroll
+        for (int q = 0; q < NT / 2; ++q) {
+            const int lo = 32 * q, hi = lo + 16;
+            f32x4 t = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                t = mma4(sR[(hi + rl) * LDR + lo + 4 * kb + g], sR[(lo + 4 * kb + g) * LDR + lo + rl], t);
+            f32x4 r21 = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) r21 = mma4(sR[(hi + rl) * LDR + hi + 4 * g + kb], t[kb], r21);
+            wave_lds_sync();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sR[(hi + rq + j) * LDR + lo + rl] = -r21[j];
+        }
+    } else {
+        if (has_prow) p_row(pm);
+        if (NT == 4 && wave >= 2) {   // the 32x32 off-diagonal block, one tile column per wave
+            const int tn = wave - 2;
+            const f32x4 Ga = kk_tile(2, tn), Gb = kk_tile(3, tn);
+            mask_a(2, tn, Ga);
+            mask_a(3, tn, Gb);
+        }
+        if (h % grp == 0) {   // K^T fragments for the scan, once per key head
+            E* KTg = reinterpret_cast<E*>(p.KT) + (((size_t)b * Hk + hk) * N + c) * S::KT_PER_CHUNK;
+            for (int f = wave - 1; f < ND * NKC; f += 3) {
+                const int dt = f / NKC, kb = f % NKC;
+                store_frag(KTg + ((size_t)f * 64 + lane) * KPL, KsT + (dt * 16 + rl) * LDT + kb * KB + kq);
             }
         }
-        if (tid < C) {   // gate factors for the scan: exp(gamma_r), then exp(gamma_last - gamma_r)
-            float* gf = p.gam + (bh * N + c) * 2 * C;
-            gf[tid] = expf(sm_gam[tid]);
-            gf[C + tid] = expf(sm_gam[C - 1] - sm_gam[tid]);
+        // zeros above the block diagonal (k-blocks of R read by phase 4 span whole blocks)
+        constexpr int CV = CP / 4;
+        for (int e = tid - 64; e < C * CV; e += kThreads - 64) {
+            const int r = e / CV, s4 = (e % CV) * 4;
+            if ((s4 >> 4) > (r >> 4)) *reinterpret_cast<float4*>(sR + r * LDR + s4) = make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        lds_barrier();   // staging, V buffers and gates are reused by the next value head
+    }
+    lds_barrier();   // (B2)
+
+    // ---- phase 3: second doubling level (32x32 blocks) -----------------------------------------
+    if constexpr (NT == 4) {
+        f32x4 t0v = zero4(), t1v = zero4();
+        const int tj = wave;   // tile column of T and R21
+        if (wave < 2) {
+            // T = A21 R11 (32 x 32, column tile tj); R11 is zero above its diagonal
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) {
+                if (kb >= 4 * tj) {
+                    const float bv = sR[(4 * kb + g) * LDR + tj * 16 + rl];
+                    t0v = mma4(sR[(32 + rl) * LDR + 4 * kb + g], bv, t0v);
+                    t1v = mma4(sR[(48 + rl) * LDR + 4 * kb + g], bv, t1v);
+                }
+            }
+        }
+        lds_barrier();   // every read of A21 is done before R21 overwrites it
+        if (wave < 2) {
+            // R21 = -R22 T; R22 rows 32..47 see T rows 0..15, rows 48..63 all of T
+            f32x4 u0 = zero4(), u1 = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                u0 = mma4(sR[(32 + rl) * LDR + 32 + 4 * g + kb], t0v[kb], u0);
+                u1 = mma4(sR[(48 + rl) * LDR + 32 + 4 * g + kb], t0v[kb], u1);
+                u1 = mma4(sR[(48 + rl) * LDR + 48 + 4 * g + kb], t1v[kb], u1);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sR[(32 + rq + j) * LDR + tj * 16 + rl] = -u0[j];
+                sR[(48 + rq + j) * LDR + tj * 16 + rl] = -u1[j];
+            }
+        }
+        lds_barrier();   // (B3) R complete
+    }
+
+    // ---- phase 4: W and Ut -------------------------------------------------------------------
+    {
+        constexpr int WPM = 4 / NT;
+        const int mt = wave % NT, part = wave / NT;
+        const int kbmax = (mt * 16 + 15) / KB;   // k-blocks past it are zero in these rows
+        frag rw[NKC], ru[NKC];
+        const float* rrow = sR + (mt * 16 + rl) * LDR + kq;
+#pragma unroll
+        for (int kb = 0; kb < NKC; ++kb) {
+            rw[kb] = X::zero();
+            ru[kb] = X::zero();
+            if (kb <= kbmax) {
+                float aw[KPL], au[KPL];
+#pragma unroll
+                for (int e = 0; e < KPL; ++e) {
+                    const float rv = rrow[kb * KB + e];
+                    aw[e] = rv * sbg[kb * KB + kq + e];
+                    au[e] = rv * sbeta[kb * KB + kq + e];
+                }
+                rw[kb] = X::ld_f(aw);
+                ru[kb] = X::ld_f(au);
+            }
+        }
+        auto wt_tile = [&](int dt) {   // W^T tile: rows dk (tile dt), columns tokens (tile mt)
+            const E* ar = KsT + (dt * 16 + rl) * LDT + kq;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < NKC; ++kb)
+                if (kb <= kbmax) acc = X::mma(X::ld(ar + kb * KB), rw[kb], acc);
+            return acc;
+        };
+        E* Wg = reinterpret_cast<E*>(p.W) + (bh * N + c) * S::W_PER_CHUNK;
+        if constexpr (KPL == 8) {
+            for (int kbp = part; kbp < NKD; kbp += WPM) {
+                const frag f = X::pack(wt_tile(2 * kbp), wt_tile(2 * kbp + 1));
+                *reinterpret_cast<frag*>(Wg + ((size_t)(mt * NKD + kbp) * 64 + lane) * KPL) = f;
+            }
+        } else {
+            for (int dt = part; dt < ND; dt += WPM) {
+                const f32x4 d = wt_tile(dt);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Wg[(size_t)(mt * NKD + 4 * dt + j) * 64 + lane] = X::from_f(d[j]);
+            }
+        }
+        E* Ug = reinterpret_cast<E*>(p.Ut) + (bh * N + c) * S::UT_PER_CHUNK;
+        for (int vt = part; vt < NV; vt += WPM) {
+            const E* br = VsT + (vt * 16 + rl) * LDT + kq;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < NKC; ++kb)
+                if (kb <= kbmax) acc = X::mma(ru[kb], X::ld(br + kb * KB), acc);
+            E ov[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ov[j] = X::from_f(acc[j]);
+            store4(Ug + (((size_t)vt * NT + mt) * 64 + lane) * 4, ov);
+        }
     }
 }
 
@@ -470,7 +565,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
     const int i0 = slice * 16;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int rl = lane & 15, kq = (lane >> 4) * KPL, rq = (lane >> 4) * 4;
+    const int rl = lane & 15, g = lane >> 4, kq = g * KPL, rq = g * 4;
     const bool chain = wave < 4;
     const int w4 = wave & 3;
     const bool has_tile = w4 < NT;
@@ -541,13 +636,14 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
         auto step = [&](const COps& op, int c) {
             const int cur = c & 1;
             if (has_tile) {
-                const E* sr = &Sb[cur][rl * LDS_ + kq];
-                const E* sl = &Sl[cur][SPLIT ? rl * LDS_ + kq : 0];
+                // W fragments hold dk in the permuted order; read S^T to match
+                const E* sr = &Sb[cur][rl * LDS_];
+                const E* sl = &Sl[cur][SPLIT ? rl * LDS_ : 0];
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int kb = 0; kb < NKD; ++kb) {
-                    acc = X::mma(op.w[kb], X::ld(sr + kb * KB), acc);
-                    if (SPLIT) acc = X::mma(op.w[kb], X::ld(sl + kb * KB), acc);
+                    acc = X::mma(op.w[kb], X::ld_perm(sr + X::poff(kb, g)), acc);
+                    if (SPLIT) acc = X::mma(op.w[kb], X::ld_perm(sl + X::poff(kb, g)), acc);
                 }
                 E u[4], us[4];
 #pragma unroll
@@ -630,7 +726,8 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
                     accq = X::mma(TAIL ? X::keep_if(op.q[kb], qok) : op.q[kb], X::ld(sr + kb * KB), accq);
                 f32x4 acc = accq * op.gr;
 #pragma unroll
-                for (int kb = 0; kb < NKC; ++kb) acc = X::mma(op.p[kb], X::ld(UT + rl * LDU + kb * KB + kq), acc);
+                for (int kb = 0; kb < NKC; ++kb)   // P fragments: tokens in the permuted order
+                    acc = X::mma(op.p[kb], X::ld_perm(UT + rl * LDU + X::poff(kb, g)), acc);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int t = t0 + m * 16 + rq + j;
@@ -664,7 +761,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
 template <typename E, int DK, int DV, int C>
 inline hipError_t launch_prefill(const PrefillParams& p, int stages, hipStream_t stream) {
     if (stages & 1) {
-        dim3 g1(p.N, p.Hk, p.B);
+        dim3 g1(p.N, p.Hv, p.B);
         intra_chunk_kernel<E, DK, DV, C><<<g1, kThreads, 0, stream>>>(p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
