@@ -9,8 +9,9 @@ in GPU memory:
     gdn_prefill_scan) so each kernel is timed with HIP events on its stream;
   * one decode token through 30 independent recurrent layers (fp32 states of
     32 x 128 x 128, N(0, 0.1^2)), as 30 back-to-back B = 1 gdn_decode_step calls.
-Inputs rotate over several buffer sets so that every step reads cold memory
-(the sets together exceed the 256 MB last-level cache).
+Before every step (outside the timed region) a 1 GiB scratch buffer is written, so
+each step starts with the L2 and the 256 MB last-level cache holding none of its data,
+and inputs also rotate over several buffer sets.
 
 value = prefill tokens per second (T / mean event time of the two prefill
 kernels).  The JSON line also carries the decode figures, the roofline of the
@@ -58,6 +59,7 @@ def kernel_source_hash():
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 COPY_CALIBRATION_BYTES = 512 << 20
+FLUSH_BYTES = 1 << 30
 
 
 def load_traffic():
@@ -94,7 +96,7 @@ def summarize_counters(fetch_dir, write_dir):
                     if row.get("Counter_Name") != counter:
                         continue
                     name = row.get("Kernel_Name", "")
-                    key = ("copy" if ("copy" in name.lower() or "elementwise" in name.lower())
+                    key = ("copy" if "copybuffer" in name.lower()
                            else "inter" if "inter_chunk_kernel" in name
                            else "intra" if "intra_chunk_kernel" in name
                            else "decode_L%d" % (int(float(row.get("Grid_Size", "0"))) // (256 * 256))
@@ -216,10 +218,15 @@ def main():
 
     nsteps = args.warmup + args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nsteps)]
+    # Written before every step, outside the timed region: evicts the L2 and the 256 MB
+    # last-level cache (the step starts cold), and keeps the GPU busy while the host enqueues
+    # the step, so the events bracket device time only, not host launch gaps.
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
 
     def step(i):
         j = i % len(sets)
         e = ev[i]
+        scratch.fill_(i & 0xFF)
         e[0].record(stream)
         check(lib.gdn_prefill_prepare(*PF[j]), "gdn_prefill_prepare")
         e[1].record(stream)

@@ -28,8 +28,8 @@
 // state is split into 16-row slices that never talk to each other.  The fp32 slice lives
 // in MFMA accumulator registers for the whole scan and is written back once at the end
 // ("Keep the recurrent state on chip": load the state once, carry it through the scan,
-// write it after).  Each chunk's operands are fetched chunks ahead into registers, so
-// the chunk-to-chunk chain waits only on LDS exchanges and matrix-core latency.
+// write it after).  Each chunk's operands are fetched chunks ahead into registers, so the
+// chunk-to-chunk chain waits only on LDS exchanges and matrix-core latency.
 //
 // Workspace layout (E = element type; a fragment is 64 lanes x KPL elements of a 16 x KB
 // operand tile, lane l holding row l % 16).  Fragments marked "permuted" hold, in lane group
@@ -39,7 +39,7 @@
 // operand in the same order.
 //   W   [B][Hv][N][C/16][DK/KB] fragments   A operand of W S^T   (rows tokens, k = dk; permuted)
 //   P   [B][Hv][N][C/16][NKC]   fragments   A operand of P U     (rows tokens, k = tokens; permuted)
-//   KT  [B][Hk][N][DK/16][NKC]  fragments   A operand of K^T U'  (rows dk,     k = tokens)
+//   KT  [B][Hk][N][DK/16][NKC]  fragments   A operand of K^T U'  (rows dk,     k = tokens; permuted)
 //   Ut  [B][Hv][N][DV/16][C/16] accumulator tiles (lane: col l % 16, rows 4 (l/16) + [0,4))
 //   gam [B][Hv][N][2][C] fp32 gate factors per chunk: exp(gamma_r), then exp(gamma_last - gamma_r)
 //       (rows past the end repeat the last row's gamma)
@@ -381,9 +381,10 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
         }
         if (h % grp == 0) {   // K^T fragments for the scan, once per key head
             E* KTg = reinterpret_cast<E*>(p.KT) + (((size_t)b * Hk + hk) * N + c) * S::KT_PER_CHUNK;
-            for (int f = wave - 1; f < ND * NKC; f += 3) {
+            for (int f = wave - 1; f < ND * NKC; f += 3) {   // tokens in the permuted order
                 const int dt = f / NKC, kb = f % NKC;
-                store_frag(KTg + ((size_t)f * 64 + lane) * KPL, KsT + (dt * 16 + rl) * LDT + kb * KB + kq);
+                *reinterpret_cast<frag*>(KTg + ((size_t)f * 64 + lane) * KPL) =
+                    X::ld_perm(KsT + (dt * 16 + rl) * LDT + X::poff(kb, g));
             }
         }
         // zeros above the block diagonal (k-blocks of R read by phase 4 span whole blocks)
@@ -495,7 +496,8 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
 // U = Ut - W S^T for their 16-token tile, then S^T <- Gamma_n S^T + K^T (e * U) for their
 // state tiles.  Output waves 4..7 compute O = Gamma (Q S^T) + P U for their token tile one
 // barrier behind, from a double-buffered copy of the state, so the output products stay off
-// the chain.  Each role prefetches its own operands NB chunks ahead into registers.
+// the chain, and write O as 16-byte pieces staged through LDS.  Each role prefetches its own
+// operands NB chunks ahead into registers.
 // SPLIT: feed the state to W S^T as a bf16 hi + lo pair (two MFMAs) so the delta U sees
 // the fp32 state to ~16 bits instead of 8.
 // ------------------------------------------------------------------------------------
@@ -551,6 +553,8 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
     __shared__ __align__(16) E Sl[2][SPLIT ? 16 * LDS_ : EPV];  // lo part
     __shared__ __align__(16) E UT[16 * LDU];                   // U^T        (for P U)
     __shared__ __align__(16) E UsT[16 * LDU];                  // (e * U)^T  (for the update)
+    constexpr int LDO = 16 + EPV;
+    __shared__ __align__(16) E Os[4][16 * LDO];                // output tile staging, per output wave
 
     // XCD-aware placement: consecutive workgroups go to different XCDs; place the slices of
     // one head on the same XCD so they share its L2 for the head's chunk operands.
@@ -634,17 +638,26 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
             }
         };
         auto step = [&](const COps& op, int c) {
+            // keeps the next step's operand uses (and so their waits) out of this one
+            __builtin_amdgcn_sched_barrier(0);
             const int cur = c & 1;
             if (has_tile) {
                 // W fragments hold dk in the permuted order; read S^T to match
                 const E* sr = &Sb[cur][rl * LDS_];
                 const E* sl = &Sl[cur][SPLIT ? rl * LDS_ : 0];
-                f32x4 acc = zero4();
+                typename X::frag sh[NKD], slo[NKD];
 #pragma unroll
                 for (int kb = 0; kb < NKD; ++kb) {
-                    acc = X::mma(op.w[kb], X::ld_perm(sr + X::poff(kb, g)), acc);
-                    if (SPLIT) acc = X::mma(op.w[kb], X::ld_perm(sl + X::poff(kb, g)), acc);
+                    sh[kb] = X::ld_perm(sr + X::poff(kb, g));
+                    if (SPLIT) slo[kb] = X::ld_perm(sl + X::poff(kb, g));
                 }
+                f32x4 acc = zero4(), accl = zero4();
+#pragma unroll
+                for (int kb = 0; kb < NKD; ++kb) {
+                    acc = X::mma(op.w[kb], sh[kb], acc);
+                    if (SPLIT) accl = X::mma(op.w[kb], slo[kb], accl);
+                }
+                if (SPLIT) acc += accl;
                 E u[4], us[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -663,7 +676,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
                     f32x4 acc = St[tw] * op.gn;
 #pragma unroll
                     for (int kb = 0; kb < NKC; ++kb)
-                        acc = X::mma(op.kt[tw][kb], X::ld(UsT + rl * LDU + kb * KB + kq), acc);
+                        acc = X::mma(op.kt[tw][kb], X::ld_perm(UsT + rl * LDU + X::poff(kb, g)), acc);
                     St[tw] = acc;
                 }
             }
@@ -715,6 +728,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
         };
         auto step = [&](const OOps& op, int c, auto tailtag) {
             constexpr bool TAIL = decltype(tailtag)::value;
+            __builtin_amdgcn_sched_barrier(0);
             const int t0 = c * C;
             lds_barrier();   // (B1) U of chunk c is in LDS; buffer (c & 1) holds chunk c's slice
             if (has_tile) {
@@ -728,11 +742,18 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
 #pragma unroll
                 for (int kb = 0; kb < NKC; ++kb)   // P fragments: tokens in the permuted order
                     acc = X::mma(op.p[kb], X::ld_perm(UT + rl * LDU + X::poff(kb, g)), acc);
+                // O tile through LDS, written as 16-byte pieces (a token's 16 state rows are
+                // sizeof(E) pieces)
+                E* os = Os[w4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int t = t0 + m * 16 + rq + j;
-                    if (!TAIL || t < T) og[((size_t)b * T + t) * Hv * DV + rl] = X::from_f(acc[j]);
-                }
+                for (int j = 0; j < 4; ++j) os[(rq + j) * LDO + rl] = X::from_f(acc[j]);
+                wave_lds_sync();
+                constexpr int PPR = (int)sizeof(E);
+                const int tok = lane / PPR, piece = lane % PPR;
+                const uint4 v = *reinterpret_cast<const uint4*>(os + tok * LDO + piece * EPV);
+                const int t = t0 + m * 16 + tok;
+                if (lane < 16 * PPR && (!TAIL || t < T))
+                    *reinterpret_cast<uint4*>(og + ((size_t)b * T + t) * Hv * DV + piece * EPV) = v;
             }
             lds_barrier();   // (B2)
         };
