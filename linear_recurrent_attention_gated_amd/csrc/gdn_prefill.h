@@ -46,6 +46,8 @@
 // NKC = ceil(C / KB); k-values past the chunk are stored as zeros.
 #pragma once
 
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -156,48 +158,83 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
     __shared__ __align__(16) float sbeta[CP];
     __shared__ __align__(16) float sbg[CP];       // beta * Gamma
 
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int T = p.T, Hk = p.Hk, Hv = p.Hv, N = p.N;
-    const int grp = Hv / Hk, hk = h / grp;
-    const int t0 = c * C;
-    const int n = min(C, T - t0);
+    const int grp = Hv / Hk;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rl = lane & 15, g = lane >> 4, kq = g * KPL, rq = g * 4;
     const size_t rsk = (size_t)Hk * DK, rsv = (size_t)Hv * DV;
-    const size_t bh = (size_t)b * Hv + h;
 
-    const E* kg = reinterpret_cast<const E*>(p.k) + ((size_t)b * T + t0) * rsk + (size_t)hk * DK;
-    const E* qg = reinterpret_cast<const E*>(p.q) + ((size_t)b * T + t0) * rsk + (size_t)hk * DK;
-    const E* vg = reinterpret_cast<const E*>(p.v) + ((size_t)b * T + t0) * rsv + (size_t)h * DV;
+    // Work items are (batch, chunk, value head).  Item i takes value head (i / 8) % grp of
+    // "rest" (i / (8 grp)) * 8 + i % 8, which names (batch, chunk, key head): with a grid that
+    // is a multiple of 8 grp, the value heads sharing a key head run at the same time on one
+    // XCD (items i and i + 8 go to workgroups 8 apart), so their K and Q rows are read once
+    // into that XCD's L2.
+    const int nrest = p.B * N * Hk;
+    const int nitems = (nrest + 7) / 8 * 8 * grp;
+    auto rest_of = [&](int i) { return (i / (8 * grp)) * 8 + i % 8; };
+    auto valid = [&](int i) { return i < nitems && rest_of(i) < nrest; };
+    struct Item { int b, c, h; };
+    auto decode = [&](int i) {
+        const int r = rest_of(i);
+        Item it;
+        it.b = r / (N * Hk);
+        it.c = (r / Hk) % N;
+        it.h = (r % Hk) * grp + (i / 8) % grp;
+        return it;
+    };
 
-    // ---- phase 0: loads (rows past the chunk's end read row n - 1 and are zeroed later) ------
+    // ---- loads of an item (rows past the chunk's end read row n - 1 and are zeroed later) ----
     constexpr int VK = DK / EPV, VV = DV / EPV;
     constexpr int PK = (C * VK + kThreads - 1) / kThreads, PV = (C * VV + kThreads - 1) / kThreads;
-    uint4 kr[PK], vr[PV];
-#pragma unroll
-    for (int i = 0; i < PK; ++i) {
-        const int idx = min(tid + i * kThreads, C * VK - 1), r = idx % C, cv = idx / C;
-        kr[i] = *reinterpret_cast<const uint4*>(kg + (size_t)min(r, n - 1) * rsk + cv * EPV);
-    }
-#pragma unroll
-    for (int i = 0; i < PV; ++i) {
-        const int idx = min(tid + i * kThreads, C * VV - 1), r = idx % C, cv = idx / C;
-        vr[i] = *reinterpret_cast<const uint4*>(vg + (size_t)min(r, n - 1) * rsv + cv * EPV);
-    }
     // this wave's P row tile: wave 0 takes row 0, wave w >= 1 row NT - w (if >= 1)
     const int pm = wave == 0 ? 0 : NT - wave;
     const bool has_prow = wave == 0 || pm >= 1;
     const int pm_ld = max(pm, 0);
+    uint4 kr[PK], vr[PV];
     frag qf[NKD];
-    {
-        const int row = pm_ld * 16 + rl;
-        const E* src = qg + (size_t)min(row, n - 1) * rsk + kq;
+    float graw, braw;
+    auto load_kvg = [&](const Item& it) {
+        const int t0 = it.c * C, n = min(C, T - t0);
+        const E* kg = reinterpret_cast<const E*>(p.k) + ((size_t)it.b * T + t0) * rsk + (size_t)(it.h / grp) * DK;
+        const E* vg = reinterpret_cast<const E*>(p.v) + ((size_t)it.b * T + t0) * rsv + (size_t)it.h * DV;
+#pragma unroll
+        for (int i = 0; i < PK; ++i) {
+            const int idx = min(tid + i * kThreads, C * VK - 1), r = idx % C, cv = idx / C;
+            kr[i] = *reinterpret_cast<const uint4*>(kg + (size_t)min(r, n - 1) * rsk + cv * EPV);
+        }
+#pragma unroll
+        for (int i = 0; i < PV; ++i) {
+            const int idx = min(tid + i * kThreads, C * VV - 1), r = idx % C, cv = idx / C;
+            vr[i] = *reinterpret_cast<const uint4*>(vg + (size_t)min(r, n - 1) * rsv + cv * EPV);
+        }
+        const size_t gidx = ((size_t)it.b * T + t0 + min(lane, n - 1)) * Hv + it.h;
+        graw = p.g[gidx];
+        braw = p.beta[gidx];
+    };
+    auto load_q = [&](const Item& it) {
+        const int t0 = it.c * C, n = min(C, T - t0);
+        const E* qg = reinterpret_cast<const E*>(p.q) + ((size_t)it.b * T + t0) * rsk + (size_t)(it.h / grp) * DK;
+        const E* src = qg + (size_t)min(pm_ld * 16 + rl, n - 1) * rsk + kq;
 #pragma unroll
         for (int kb = 0; kb < NKD; ++kb) qf[kb] = X::ld(src + kb * KB);
-    }
-    const size_t gidx = ((size_t)b * T + t0 + min(lane, n - 1)) * Hv + h;
-    const float graw = p.g[gidx], braw = p.beta[gidx];
+    };
+
+    int item = blockIdx.x;
+    if (!valid(item)) return;
+    Item cur = decode(item);
+    load_kvg(cur);
+    load_q(cur);
+    for (;;) {
+    const int c = cur.c, h = cur.h, b = cur.b;
+    const int hk = h / grp;
+    const int t0 = c * C;
+    const int n = min(C, T - t0);
+    const size_t bh = (size_t)b * Hv + h;
+    // the next item's loads are issued while this one is computed
+    const int next = item + (int)gridDim.x;
+    const bool more = valid(next);
+    const Item nxt = decode(more ? next : item);
 
     // ---- phase 1: K rows, K^T and V^T into LDS; gates -----------------------------------------
 #pragma unroll
@@ -253,6 +290,7 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
             gf[C + lane] = exp2f(gl2 - x2);
         }
     }
+    load_kvg(nxt);   // registers consumed above; the next item's rows are in flight from here
 #pragma unroll
     for (int kb = 0; kb < NKD; ++kb) qf[kb] = X::keep_if(qf[kb], pm_ld * 16 + rl < n);
     lds_barrier();   // (B1)
@@ -325,6 +363,7 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
 #pragma unroll
         for (int q = 0; q < NT / 2; ++q) G1[q] = kk_tile(2 * q + 1, 2 * q);
         p_row(0);
+        load_q(nxt);
 #pragma unroll
         for (int d = 0; d < NT; ++d) mask_a(d, d, Gd[d]);
 #pragma unroll
@@ -373,6 +412,7 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
         }
     } else {
         if (has_prow) p_row(pm);
+        load_q(nxt);
         if (NT == 4 && wave >= 2) {   // the 32x32 off-diagonal block, one tile column per wave
             const int tn = wave - 2;
             const f32x4 Ga = kk_tile(2, tn), Gb = kk_tile(3, tn);
@@ -486,6 +526,11 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
             for (int j = 0; j < 4; ++j) ov[j] = X::from_f(acc[j]);
             store4(Ug + (((size_t)vt * NT + mt) * 64 + lane) * 4, ov);
         }
+    }
+    if (!more) break;
+    lds_barrier();   // this item's LDS reads are done before the next item overwrites it
+    item = next;
+    cur = nxt;
     }
 }
 
@@ -778,12 +823,36 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
     }
 }
 
+// Workgroups of the intra kernel that fit on the current device at once (the kernel loops
+// over its work items, so it is launched with exactly that many), cached per device.
+template <typename E, int DK, int DV, int C>
+inline int intra_capacity() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int cap = cache[dev].load(std::memory_order_relaxed);
+    if (cap == 0) {
+        int ncu = 0, per = 0;
+        if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) ncu = 1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, intra_chunk_kernel<E, DK, DV, C>, kThreads, 0) !=
+            hipSuccess)
+            per = 1;
+        cap = std::max(1, ncu) * std::max(1, per);
+        cache[dev].store(cap, std::memory_order_relaxed);
+    }
+    return cap;
+}
+
 // stage bit 1: intra-chunk kernel; bit 2: inter-chunk kernel.
 template <typename E, int DK, int DV, int C>
 inline hipError_t launch_prefill(const PrefillParams& p, int stages, hipStream_t stream) {
     if (stages & 1) {
-        dim3 g1(p.N, p.Hv, p.B);
-        intra_chunk_kernel<E, DK, DV, C><<<g1, kThreads, 0, stream>>>(p);
+        // grid: a multiple of 8 (Hv / Hk) workgroups (see the work-item order), at most the
+        // resident capacity and at most the number of work items
+        const int unit = 8 * (p.Hv / p.Hk);
+        const int nitems = (p.B * p.N * p.Hk + 7) / 8 * 8 * (p.Hv / p.Hk);
+        const int grid = std::min(nitems, std::max(unit, intra_capacity<E, DK, DV, C>() / unit * unit));
+        intra_chunk_kernel<E, DK, DV, C><<<grid, kThreads, 0, stream>>>(p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
