@@ -106,6 +106,30 @@ __device__ __forceinline__ void store4(E* dst, const E* v) {
     else *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(v);
 }
 
+// np (1, 2, 4 or 8; a compile-time constant after inlining) consecutive elements to dst, in
+// the widest pieces its alignment (np * sizeof(E) bytes, or 16) allows
+template <typename E>
+__device__ __forceinline__ void store_run(E* dst, const E (&v)[8], int np) {
+    const int bytes = np * (int)sizeof(E);
+    if (bytes >= 16) {
+        for (int o = 0; o < np; o += 16 / (int)sizeof(E)) {
+            uint4 u;
+            __builtin_memcpy(&u, v + o, 16);
+            *reinterpret_cast<uint4*>(dst + o) = u;
+        }
+    } else if (bytes == 8) {
+        uint2 u;
+        __builtin_memcpy(&u, v, 8);
+        *reinterpret_cast<uint2*>(dst) = u;
+    } else if (bytes == 4) {
+        uint32_t u;
+        __builtin_memcpy(&u, v, 4);
+        *reinterpret_cast<uint32_t*>(dst) = u;
+    } else {
+        dst[0] = v[0];
+    }
+}
+
 // ------------------------------------------------------------------------------------
 // Kernel 1: per-chunk, state-independent blocks; one workgroup per (batch, value head,
 // chunk), four waves.
@@ -198,14 +222,15 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
         const int t0 = it.c * C, n = min(C, T - t0);
         const E* kg = reinterpret_cast<const E*>(p.k) + ((size_t)it.b * T + t0) * rsk + (size_t)(it.h / grp) * DK;
         const E* vg = reinterpret_cast<const E*>(p.v) + ((size_t)it.b * T + t0) * rsv + (size_t)it.h * DV;
+        // thread tid holds vectors tid * PK + [0, PK): PK consecutive tokens of one column block
 #pragma unroll
         for (int i = 0; i < PK; ++i) {
-            const int idx = min(tid + i * kThreads, C * VK - 1), r = idx % C, cv = idx / C;
+            const int idx = min(tid * PK + i, C * VK - 1), r = idx % C, cv = idx / C;
             kr[i] = *reinterpret_cast<const uint4*>(kg + (size_t)min(r, n - 1) * rsk + cv * EPV);
         }
 #pragma unroll
         for (int i = 0; i < PV; ++i) {
-            const int idx = min(tid + i * kThreads, C * VV - 1), r = idx % C, cv = idx / C;
+            const int idx = min(tid * PV + i, C * VV - 1), r = idx % C, cv = idx / C;
             vr[i] = *reinterpret_cast<const uint4*>(vg + (size_t)min(r, n - 1) * rsv + cv * EPV);
         }
         const size_t gidx = ((size_t)it.b * T + t0 + min(lane, n - 1)) * Hv + it.h;
@@ -237,30 +262,40 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
     const Item nxt = decode(more ? next : item);
 
     // ---- phase 1: K rows, K^T and V^T into LDS; gates -----------------------------------------
+    // rows to Ks; the transposes take each thread's PK consecutive tokens of a column as one
+    // contiguous run per column
+    auto to_lds = [&](const uint4 (&rv)[cmax(PK, PV)], int np, int nvec, E* rows, E* trans) {
+        if (tid * np < nvec) {
+            const int r0 = (tid * np) % C, cv = (tid * np) / C;
+            E el[8][EPV];
 #pragma unroll
-    for (int i = 0; i < PK; ++i) {
-        const int idx = tid + i * kThreads;
-        if (idx < C * VK) {
-            const int r = idx % C, cv = idx / C;
-            const uint4 z = {0u, 0u, 0u, 0u};
-            const uint4 a = r < n ? kr[i] : z;
-            *reinterpret_cast<uint4*>(Ks + r * LDK + cv * EPV) = a;
-            const E* e = reinterpret_cast<const E*>(&a);
+            for (int i = 0; i < 8; ++i) {
+                if (i >= np) break;
+                const uint4 z = {0u, 0u, 0u, 0u};
+                const uint4 a = r0 + i < n ? rv[i] : z;
+                if (rows) *reinterpret_cast<uint4*>(rows + (r0 + i) * LDK + cv * EPV) = a;
+                const E* e = reinterpret_cast<const E*>(&a);
 #pragma unroll
-            for (int j = 0; j < EPV; ++j) KsT[(cv * EPV + j) * LDT + r] = e[j];
+                for (int j = 0; j < EPV; ++j) el[i][j] = e[j];
+            }
+#pragma unroll
+            for (int j = 0; j < EPV; ++j) {
+                E run[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) run[i] = el[i][j];
+                store_run(trans + (cv * EPV + j) * LDT + r0, run, np);
+            }
         }
-    }
+    };
+    {
+        uint4 kk[cmax(PK, PV)], vv[cmax(PK, PV)];
 #pragma unroll
-    for (int i = 0; i < PV; ++i) {
-        const int idx = tid + i * kThreads;
-        if (idx < C * VV) {
-            const int r = idx % C, cv = idx / C;
-            const uint4 z = {0u, 0u, 0u, 0u};
-            const uint4 a = r < n ? vr[i] : z;
-            const E* e = reinterpret_cast<const E*>(&a);
-#pragma unroll
-            for (int j = 0; j < EPV; ++j) VsT[(cv * EPV + j) * LDT + r] = e[j];
+        for (int i = 0; i < cmax(PK, PV); ++i) {
+            kk[i] = kr[min(i, PK - 1)];
+            vv[i] = vr[min(i, PV - 1)];
         }
+        to_lds(kk, PK, C * VK, Ks, KsT);
+        to_lds(vv, PV, C * VV, nullptr, VsT);
     }
     if (CP > C) {   // token columns past the chunk (16-token chunks in bf16)
         for (int e = tid; e < (DK + DV) * (CP - C); e += kThreads) {
