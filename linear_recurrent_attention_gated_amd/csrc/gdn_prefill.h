@@ -150,6 +150,10 @@ __device__ __forceinline__ void store_run(E* dst, const E (&v)[8], int np) {
 // ------------------------------------------------------------------------------------
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+// 2^x with the hardware instruction (results below the fp32 normal range flush to zero,
+// which is what the decay factors that use it need)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // wave-local ordering point for LDS traffic exchanged between lanes of one wave
 __device__ __forceinline__ void wave_lds_sync() {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -349,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = tm * 16 + rq + j;
-            sR[r * LDR + s] = (s < r) ? brv[j] * exp2f(grv[j] - gs) * G[j] : 0.f;
+            sR[r * LDR + s] = (s < r) ? brv[j] * fast_exp2(grv[j] - gs) * G[j] : 0.f;
         }
     };
     // P row tile m: P[r][s] = exp(gamma_r - gamma_s) (q_r . k_s), s <= r, stored as permuted
@@ -369,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int s = t * 16 + rq + j;
-                    acc[j] = (s <= r) ? exp2f(gr - gsv[j]) * acc[j] : 0.f;
+                    acc[j] = (s <= r) ? fast_exp2(gr - gsv[j]) * acc[j] : 0.f;
                 }
             }
             return acc;
