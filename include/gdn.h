@@ -61,14 +61,15 @@ typedef enum {
     GDN_ERR_UNSUPPORTED = 3, /* dk, dv, chunk or dtype outside the supported set            */
     GDN_ERR_ALIGN = 4,       /* a pointer violates the alignment rules above                */
     GDN_ERR_ALIAS = 5,       /* an output overlaps another argument (state_out == state_in is allowed) */
-    GDN_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than gdn_prefill_workspace_bytes  */
+    GDN_ERR_WORKSPACE = 6,   /* workspace NULL, or too small (see gdn_prefill)              */
     GDN_ERR_HIP = 7          /* the HIP runtime reported an error while enqueueing          */
 } gdn_status;
 
-/* Bytes of device workspace gdn_prefill needs for these sizes (0 when T == 0).  Returns 0
- * also for unsupported arguments (gdn_prefill then reports the reason).  The workspace
- * holds the per-chunk blocks of the blockwise form between its two kernels; its content
- * on entry is irrelevant and on exit unspecified. */
+/* Bytes of device workspace gdn_prefill needs to run these sizes in one pass (0 when
+ * T == 0).  Returns 0 also for unsupported arguments (gdn_prefill then reports the reason).
+ * The workspace holds the per-chunk blocks of the blockwise form between its two kernels;
+ * its content on entry is irrelevant and on exit unspecified.  It grows linearly with B * T
+ * (about 97 MiB at B = 1, T = 4096, Hk = 16, Hv = 32, dk = dv = 128, bf16). */
 size_t gdn_prefill_workspace_bytes(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                                    gdn_dtype dtype);
 
@@ -79,8 +80,16 @@ size_t gdn_prefill_workspace_bytes(int B, int T, int Hk, int Hv, int dk, int dv,
  *   o          [B, T, Hv, dv] dtype      (o_t = S_t q_t, the post-update state read with q_t)
  *   state_out  [B, Hv, dv, dk] float     (state after token T-1; may equal state_in, which
  *                                         is then updated in place)
- *   workspace  device buffer of at least gdn_prefill_workspace_bytes(...) bytes; may be
- *              NULL only when T == 0.
+ *   workspace  device buffer, 256-byte aligned; may be NULL only when T == 0.  With
+ *              gdn_prefill_workspace_bytes(...) bytes the prompt runs in one pass.  A
+ *              smaller workspace bounds the temporary memory instead: the prompt is run
+ *              in consecutive segments of the longest whole number of chunks whose
+ *              workspace fits, and the state is carried from one to the next through
+ *              state_out ("Optimizing on-device inference for Apple Silicon", section
+ *              "Bound temporary memory with prompt chunking": segmenting a prompt and
+ *              carrying the recurrent state leaves the output unchanged).  The result
+ *              equals the one-pass result bit for bit.  GDN_ERR_WORKSPACE if not even one
+ *              chunk fits.
  * T == 0 copies state_in (or zeros) to state_out and touches nothing else.
  * Outputs must not overlap each other, the inputs or the workspace, except
  * state_out == state_in exactly. */
@@ -91,8 +100,9 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
 
 /* The two stages of gdn_prefill, for callers that schedule them separately (for example
  * to overlap the state-independent stage of one segment with other work, or to time each
- * stage).  Same arguments and rules as gdn_prefill; gdn_prefill == prepare then scan on
- * one stream with one workspace.
+ * stage).  Same arguments and rules as gdn_prefill, except that they need the one-pass
+ * workspace (gdn_prefill_workspace_bytes); gdn_prefill == prepare then scan on one stream
+ * with one workspace.
  *   gdn_prefill_prepare: the state-independent per-chunk blocks (decay-masked Gram, the
  *     unit-triangular inverse, the W / U~ blocks, the masked query-key block), written to
  *     the workspace.  Reads q, k, v, g, beta; ignores state_in, o and state_out (they

@@ -108,29 +108,50 @@ gdn_status prefill_stages(const void* q, const void* k, const void* v, const flo
         return gdn::copy_state(state_in, state_out, (size_t)B * Hv * dv * dk, st) == hipSuccess
                    ? GDN_OK : GDN_ERR_HIP;
     }
-    const Layout L = layout(B, T, Hk, Hv, dk, dv, chunk, dtype);
-    if (!workspace || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
+    if (!workspace) return GDN_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
-
-    gdn::PrefillParams p;
-    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.state_in = state_in;
-    p.o = o; p.state_out = state_out;
-    char* ws = static_cast<char*>(workspace);
-    p.W = ws + L.W; p.Ut = ws + L.Ut; p.P = ws + L.P; p.KT = ws + L.KT;
-    p.gam = reinterpret_cast<float*>(ws + L.gam);
-    p.B = B; p.T = T; p.Hk = Hk; p.Hv = Hv; p.N = (T + chunk - 1) / chunk;
-
-    hipError_t e = hipErrorInvalidValue;
-    if (dtype == GDN_BF16) {
-        if (chunk == 16) e = gdn::prefill_bf16_c16(dk, dv, p, stages, st);
-        else if (chunk == 32) e = gdn::prefill_bf16_c32(dk, dv, p, stages, st);
-        else e = gdn::prefill_bf16_c64(dk, dv, p, stages, st);
-    } else {
-        if (chunk == 16) e = gdn::prefill_f32_c16(dk, dv, p, stages, st);
-        else if (chunk == 32) e = gdn::prefill_f32_c32(dk, dv, p, stages, st);
-        else e = gdn::prefill_f32_c64(dk, dv, p, stages, st);
+    // Tokens per pass: the whole prompt when the workspace holds it, otherwise (full prefill
+    // only) the longest whole number of chunks whose workspace fits; the passes then carry
+    // the state through state_out.
+    int seg = T;
+    if (layout(B, T, Hk, Hv, dk, dv, chunk, dtype).total > workspace_bytes) {
+        if (stages != 3) return GDN_ERR_WORKSPACE;
+        int lo = 0, hi = (T + chunk - 1) / chunk;   // chunks per pass: lo fits, hi does not
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) / 2;
+            if (layout(B, mid * chunk, Hk, Hv, dk, dv, chunk, dtype).total <= workspace_bytes) lo = mid;
+            else hi = mid;
+        }
+        if (lo == 0) return GDN_ERR_WORKSPACE;
+        seg = lo * chunk;
     }
-    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+
+    for (int t0 = 0; t0 < T; t0 += seg) {
+        const int Tp = T - t0 < seg ? T - t0 : seg;
+        const Layout L = layout(B, Tp, Hk, Hv, dk, dv, chunk, dtype);
+        gdn::PrefillParams p;
+        p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+        p.state_in = t0 == 0 ? state_in : state_out;
+        p.o = o; p.state_out = state_out;
+        char* ws = static_cast<char*>(workspace);
+        p.W = ws + L.W; p.Ut = ws + L.Ut; p.P = ws + L.P; p.KT = ws + L.KT;
+        p.gam = reinterpret_cast<float*>(ws + L.gam);
+        p.B = B; p.T = Tp; p.Hk = Hk; p.Hv = Hv; p.N = (Tp + chunk - 1) / chunk;
+        p.Ts = T; p.t0 = t0;
+
+        hipError_t e = hipErrorInvalidValue;
+        if (dtype == GDN_BF16) {
+            if (chunk == 16) e = gdn::prefill_bf16_c16(dk, dv, p, stages, st);
+            else if (chunk == 32) e = gdn::prefill_bf16_c32(dk, dv, p, stages, st);
+            else e = gdn::prefill_bf16_c64(dk, dv, p, stages, st);
+        } else {
+            if (chunk == 16) e = gdn::prefill_f32_c16(dk, dv, p, stages, st);
+            else if (chunk == 32) e = gdn::prefill_f32_c32(dk, dv, p, stages, st);
+            else e = gdn::prefill_f32_c64(dk, dv, p, stages, st);
+        }
+        if (e != hipSuccess) return GDN_ERR_HIP;
+    }
+    return GDN_OK;
 }
 
 }  // namespace

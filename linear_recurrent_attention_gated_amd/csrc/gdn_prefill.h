@@ -68,7 +68,11 @@ struct PrefillParams {
     void* P;
     void* KT;
     float* gam;   // gate factors (see the workspace layout)
-    int B, T, Hk, Hv, N;  // N = number of chunks
+    int B, T, Hk, Hv, N;  // T = tokens of this pass, N = its number of chunks
+    // Token t of batch b of this pass is token Ts * b + t0 + t of q, k, v, g, beta and o
+    // (Ts = the arrays' tokens per batch, t0 = first token of the pass).  A prompt run in
+    // several passes carries the state between them through state_out.
+    int Ts, t0;
 };
 
 constexpr int kThreads = 256;
@@ -224,8 +228,8 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
     float graw, braw;
     auto load_kvg = [&](const Item& it) {
         const int t0 = it.c * C, n = min(C, T - t0);
-        const E* kg = reinterpret_cast<const E*>(p.k) + ((size_t)it.b * T + t0) * rsk + (size_t)(it.h / grp) * DK;
-        const E* vg = reinterpret_cast<const E*>(p.v) + ((size_t)it.b * T + t0) * rsv + (size_t)it.h * DV;
+        const E* kg = reinterpret_cast<const E*>(p.k) + ((size_t)it.b * p.Ts + p.t0 + t0) * rsk + (size_t)(it.h / grp) * DK;
+        const E* vg = reinterpret_cast<const E*>(p.v) + ((size_t)it.b * p.Ts + p.t0 + t0) * rsv + (size_t)it.h * DV;
         // thread tid holds vectors tid * PK + [0, PK): PK consecutive tokens of one column block
 #pragma unroll
         for (int i = 0; i < PK; ++i) {
@@ -237,13 +241,13 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
             const int idx = min(tid * PV + i, C * VV - 1), r = idx % C, cv = idx / C;
             vr[i] = *reinterpret_cast<const uint4*>(vg + (size_t)min(r, n - 1) * rsv + cv * EPV);
         }
-        const size_t gidx = ((size_t)it.b * T + t0 + min(lane, n - 1)) * Hv + it.h;
+        const size_t gidx = ((size_t)it.b * p.Ts + p.t0 + t0 + min(lane, n - 1)) * Hv + it.h;
         graw = p.g[gidx];
         braw = p.beta[gidx];
     };
     auto load_q = [&](const Item& it) {
         const int t0 = it.c * C, n = min(C, T - t0);
-        const E* qg = reinterpret_cast<const E*>(p.q) + ((size_t)it.b * T + t0) * rsk + (size_t)(it.h / grp) * DK;
+        const E* qg = reinterpret_cast<const E*>(p.q) + ((size_t)it.b * p.Ts + p.t0 + t0) * rsk + (size_t)(it.h / grp) * DK;
         const E* src = qg + (size_t)min(pm_ld * 16 + rl, n - 1) * rsk + kq;
 #pragma unroll
         for (int kb = 0; kb < NKD; ++kb) qf[kb] = X::ld(src + kb * KB);
@@ -803,7 +807,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
             const int t0 = c * C;
             op.gr = *reinterpret_cast<const f32x4*>(gates + (size_t)c * 2 * C + m * 16 + rq);
             const int tq = t0 + m * 16 + rl;
-            const E* qsrc = qg + ((size_t)b * T + min(tq, T - 1)) * Hk * DK + kq;
+            const E* qsrc = qg + ((size_t)b * p.Ts + p.t0 + min(tq, T - 1)) * Hk * DK + kq;
 #pragma unroll
             for (int kb = 0; kb < NKD; ++kb) op.q[kb] = X::ld(qsrc + kb * KB);   // rows past T: zeroed in the tail
             const E* psrc = Pg + (size_t)c * Sh::P_PER_CHUNK + (size_t)m * NKC * Sh::FRAG + lane * KPL;
@@ -837,7 +841,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
                 const uint4 v = *reinterpret_cast<const uint4*>(os + tok * LDO + piece * EPV);
                 const int t = t0 + m * 16 + tok;
                 if (lane < 16 * PPR && (!TAIL || t < T))
-                    *reinterpret_cast<uint4*>(og + ((size_t)b * T + t) * Hv * DV + piece * EPV) = v;
+                    *reinterpret_cast<uint4*>(og + ((size_t)b * p.Ts + p.t0 + t) * Hv * DV + piece * EPV) = v;
             }
             lds_barrier();   // (B2)
         };

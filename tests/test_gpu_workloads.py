@@ -201,3 +201,45 @@ def test_bitwise_deterministic():
     o1, s1 = gpu_prefill(d, 64, d["state"])
     o2, s2 = gpu_prefill(d, 64, d["state"])
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def _prefill_with_workspace(d, chunk, nbytes, state=None):
+    dd = to_dev(d)
+    B, T, Hk, dk = dd["q"].shape
+    Hv, dv = dd["v"].shape[2], dd["v"].shape[3]
+    o = torch.empty((B, T, Hv, dv), dtype=dd["q"].dtype, device="cuda")
+    s_out = torch.empty((B, Hv, dv, dk), dtype=torch.float32, device="cuda")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    st = None if state is None else torch.as_tensor(np.asarray(state, np.float32)).cuda()
+    gdn.gdn_prefill(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], st, o, s_out, chunk, ws)
+    torch.cuda.synchronize()
+    return o, s_out
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("chunk,seg_chunks", [(64, 1), (64, 3), (32, 5), (16, 7)])
+def test_segmented_prefill_equals_one_pass(dt, chunk, seg_chunks):
+    # "Bound temporary memory with prompt chunking": a workspace that holds only seg_chunks
+    # chunks makes gdn_prefill run the prompt in segments, carrying the state between them;
+    # every chunk computation is the same as in one pass, so the result is identical
+    d = make_inputs(2, 1000, 2, 4, 128, 128, seed=26, state_std=0.1, dtype=dt)
+    full = gdn.gdn_prefill_workspace_bytes(2, 1000, 2, 4, 128, 128, chunk, dt)
+    small = gdn.gdn_prefill_workspace_bytes(2, seg_chunks * chunk, 2, 4, 128, 128, chunk, dt)
+    assert small < full
+    say("segmented", dt, chunk, seg_chunks)
+    o1, s1 = _prefill_with_workspace(d, chunk, full, d["state"])
+    o2, s2 = _prefill_with_workspace(d, chunk, small, d["state"])
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    o_ref, s_ref = oracle_prefill(d, d["state"])
+    assert nrel(np32(o2), o_ref) < TOL_O and nrel(s2.cpu().numpy(), s_ref) < TOL_S
+
+
+def test_long_128k_bounded_workspace(c4):
+    # the 131072-token prompt with a 256 MiB workspace (the one-pass workspace is ~3 GiB)
+    d, o_full, s_full = c4
+    w = LONG_128K
+    full = gdn.gdn_prefill_workspace_bytes(w.B, w.T, w.Hk, w.Hv, w.dk, w.dv, w.chunk, torch.bfloat16)
+    assert full > 8 * (256 << 20)
+    say("long 128k, bounded workspace")
+    o, s = _prefill_with_workspace(d, w.chunk, 256 << 20)
+    assert np.array_equal(np32(o), o_full) and np.array_equal(s.cpu().numpy(), s_full)
