@@ -33,6 +33,12 @@
  * widened to double exactly.  An fp32 twin exists only to measure how large the
  * rounding drift of a single-precision scan is.
  *
+ * Normalised variant.  The same pages' section "Reduce intermediate and state traffic"
+ * fuses the query/key preparation into the kernels that follow it.  That preparation is
+ * read here as per-head L2 normalisation, the form Gated DeltaNet gives q and k:
+ *     x <- x / sqrt(sum_j x_j^2 + 1e-6)          (eps keeps a zero vector finite)
+ * applied to k_t and q_t in fp64 after widening, before the update above.
+ *
  * Layouts (contiguous, row-major):
  *   q, k      [B, T, Hk, dk]      v        [B, T, Hv, dv]
  *   g, beta   [B, T, Hv]          state_in [B, Hv, dv, dk] (NULL = zero state)
@@ -56,7 +62,19 @@ typedef struct {
     pthread_mutex_t lock;
     void *o_sel, *s_sel;   /* double* or float* */
     int use_f32;
+    int qk_norm;           /* normalise k_t and q_t first (fp64 scan only) */
 } job_t;
+
+#define GDN_ORACLE_NORM_EPS 1e-6
+
+/* x <- x / sqrt(|x|^2 + eps), in place */
+static void l2_normalise(double *x, int n)
+{
+    double ss = 0.0;
+    for (int j = 0; j < n; ++j) ss += x[j] * x[j];
+    const double inv = 1.0 / sqrt(ss + GDN_ORACLE_NORM_EPS);
+    for (int j = 0; j < n; ++j) x[j] *= inv;
+}
 
 /* One work item: rows [r0, r1) of the state of pair sel[2*p], sel[2*p+1]. */
 static void run_item_f64(job_t *J, int p, int r0, int r1)
@@ -81,6 +99,7 @@ static void run_item_f64(job_t *J, int p, int r0, int r1)
             const double bt = (double)J->beta[tok * Hv + h];
             const double vi = (double)J->v[(tok * Hv + h) * dv + i];
             for (int j = 0; j < dk; ++j) { kk[j] = (double)kt[j]; qq[j] = (double)qt[j]; }
+            if (J->qk_norm) { l2_normalise(kk, dk); l2_normalise(qq, dk); }
             double u = 0.0;                       /* (S_{t-1} k_t)[i] */
             for (int j = 0; j < dk; ++j) u += S[j] * kk[j];
             const double delta = bt * (vi - a * u);
@@ -189,6 +208,21 @@ int gdn_oracle_seq_f64(const float *q, const float *k, const float *v, const flo
     J.sel = sel; J.n_sel = n_sel; J.o_sel = o_sel; J.s_sel = s_sel;
     J.B = B; J.T = T; J.Hk = Hk; J.Hv = Hv; J.dk = dk; J.dv = dv;
     J.rows_per_item = rows_per_item; J.use_f32 = 0;
+    return run(&J, nthreads);
+}
+
+/* fp64 sequential scan with q_t and k_t L2-normalised first (see the header). */
+int gdn_oracle_seq_f64_qknorm(const float *q, const float *k, const float *v, const float *g,
+                              const float *beta, const double *state_in, const int *sel,
+                              int n_sel, double *o_sel, double *s_sel, int B, int T, int Hk,
+                              int Hv, int dk, int dv, int nthreads, int rows_per_item)
+{
+    job_t J;
+    memset(&J, 0, sizeof(J));
+    J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.state_in = state_in;
+    J.sel = sel; J.n_sel = n_sel; J.o_sel = o_sel; J.s_sel = s_sel;
+    J.B = B; J.T = T; J.Hk = Hk; J.Hv = Hv; J.dk = dk; J.dv = dv;
+    J.rows_per_item = rows_per_item; J.use_f32 = 0; J.qk_norm = 1;
     return run(&J, nthreads);
 }
 

@@ -33,6 +33,10 @@ chunked       the blockwise evaluation: per chunk, the decay-masked key Gram
               dense step at a time, to check the chunk algebra the GPU uses.
 decode_step   one token of the recurrence (the T = 1 scan) on a given state.
 
+seq and decode_step take qk_norm=True for the fused query/key preparation of
+section "Reduce intermediate and state traffic", read as per-head L2
+normalisation of q_t and k_t, x / sqrt(|x|^2 + 1e-6), done in fp64 first.
+
 Every input array is widened exactly to float64 before use.  Layouts: q, k
 [B,T,Hk,dk]; v [B,T,Hv,dv]; g, beta [B,T,Hv]; state [B,Hv,dv,dk]; o [B,T,Hv,dv].
 
@@ -57,8 +61,7 @@ def _lib():
             from . import build as _b  # noqa: WPS433 (lazy: build only when absent)
             _b.build_oracle()
         lib = ctypes.CDLL(path)
-        for name, otype in (("gdn_oracle_seq_f64", ctypes.c_double),
-                            ("gdn_oracle_seq_f32", ctypes.c_float)):
+        for name in ("gdn_oracle_seq_f64", "gdn_oracle_seq_f64_qknorm", "gdn_oracle_seq_f32"):
             fn = getattr(lib, name)
             P = ctypes.c_void_p
             fn.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, P, P] + [ctypes.c_int] * 8
@@ -114,12 +117,15 @@ def _run_c(fname, out_dtype, q, k, v, g, beta, state_in, pairs, nthreads, rows_p
     return sel, o, s
 
 
-def seq(q, k, v, g, beta, state_in=None, pairs=None, nthreads=None, rows_per_item=16):
+def seq(q, k, v, g, beta, state_in=None, pairs=None, nthreads=None, rows_per_item=16,
+        qk_norm=False):
     """fp64 sequential scan (C).  Returns (o [B,T,Hv,dv], state [B,Hv,dv,dk]) when
     ``pairs`` is None, else (o_sel [n,T,dv], s_sel [n,dv,dk]) for the listed
-    (b, h) pairs only -- each pair is an independent recurrence."""
-    sel, o, s = _run_c("gdn_oracle_seq_f64", np.float64, q, k, v, g, beta, state_in, pairs,
-                       nthreads, rows_per_item)
+    (b, h) pairs only -- each pair is an independent recurrence.  qk_norm: every
+    q_t and k_t is first replaced by x / sqrt(|x|^2 + 1e-6) in fp64."""
+    fname = "gdn_oracle_seq_f64_qknorm" if qk_norm else "gdn_oracle_seq_f64"
+    sel, o, s = _run_c(fname, np.float64, q, k, v, g, beta, state_in, pairs, nthreads,
+                       rows_per_item)
     if pairs is not None:
         return o, s
     B, T, _, Hv, dk, dv = _dims(q, k, v, g, beta)
@@ -210,11 +216,11 @@ def chunked(q, k, v, g, beta, state_in=None, chunk=16):
     return o, S_all
 
 
-def decode_step(q, k, v, g, beta, state):
+def decode_step(q, k, v, g, beta, state, qk_norm=False):
     """One token of the recurrence (fp64, C scan) on the given state.
 
     q, k [B,Hk,dk]; v [B,Hv,dv]; g, beta [B,Hv]; state [B,Hv,dv,dk].
     Returns (o [B,Hv,dv], new_state [B,Hv,dv,dk])."""
     q, k, v, g, beta = (np.asarray(x)[:, None] for x in (q, k, v, g, beta))
-    o, s = seq(q, k, v, g, beta, state_in=state)
+    o, s = seq(q, k, v, g, beta, state_in=state, qk_norm=qk_norm)
     return o[:, 0], s

@@ -306,3 +306,55 @@ def test_decode_step_is_one_token_of_the_scan():
     o, s = orc.decode_step(q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0], S0)
     o2, s2 = orc.seq_literal(q, k, v, g, beta, S0)
     assert rel(o, o2[:, 0]) < 1e-13 and rel(s, s2) < 1e-13
+
+
+# --- P13: fused query/key L2 normalisation (qk_norm) -----------------------------------------
+# Read of section "Reduce intermediate and state traffic" (the query/key preparation fused
+# into the update): q_t, k_t -> x / sqrt(|x|^2 + 1e-6) before the recurrence.
+
+def _pow2_scaled(x, rng, lo=0, hi=5):
+    """x with each token's vector multiplied by a random power of two (exact in fp32)."""
+    e = rng.integers(lo, hi, size=x.shape[:-1] + (1,))
+    return (x * np.exp2(e)).astype(np.float32)
+
+
+def test_p13_qknorm_write_then_read_raw_keys():
+    # beta = 1 and q_t = k_t of any length: after normalisation |k^_t| = 1 - O(eps / |k|^2),
+    # so o_t = S_t k^_t = v_t whatever a_t and S_{t-1} are.  Unnormalised keys of length
+    # 1..16 would return up to 256 v_t, so a missing q or k normalisation fails here.
+    rng = np.random.default_rng(31)
+    q, k, v, g, beta, S0 = rand_inputs(31, B=2, T=10, Hk=1, Hv=2, state=True, g_scale=2.0)
+    kr = _pow2_scaled(k, rng)
+    beta[:] = 1.0
+    o, _ = orc.seq(kr, kr, v, g, beta, S0, qk_norm=True)
+    np.testing.assert_allclose(o, v.astype(np.float64), atol=5e-6)
+    od, _ = orc.decode_step(kr[:, 3], kr[:, 3], v[:, 3], g[:, 3], beta[:, 3], S0, qk_norm=True)
+    np.testing.assert_allclose(od, v[:, 3].astype(np.float64), atol=5e-6)
+
+
+def test_p13_qknorm_scale_invariance():
+    # positive per-token rescaling of q and k does not change the result (to eps / |x|^2)
+    rng = np.random.default_rng(32)
+    q, k, v, g, beta, S0 = rand_inputs(32, B=1, T=14, Hk=2, Hv=4, unit=False, state=True)
+    o1, s1 = orc.seq(q, k, v, g, beta, S0, qk_norm=True)
+    o2, s2 = orc.seq(_pow2_scaled(q, rng, -2, 4), _pow2_scaled(k, rng, -2, 4), v, g, beta, S0,
+                     qk_norm=True)
+    assert rel(o2, o1) < 1e-5 and rel(s2, s1) < 1e-5
+    # and unit-length inputs are left (almost) unchanged
+    qu, ku, *_ = rand_inputs(33, B=1, T=14, Hk=2, Hv=4, unit=True)
+    o3, s3 = orc.seq(qu, ku, v, g, beta, S0, qk_norm=True)
+    o4, s4 = orc.seq(qu, ku, v, g, beta, S0)
+    assert rel(o3, o4) < 1e-5 and rel(s3, s4) < 1e-5
+
+
+def test_p13_qknorm_zero_vectors_stay_finite():
+    # k_t = 0 leaves only the decay (S_t = a_t S_{t-1}); q_t = 0 reads o_t = 0
+    q, k, v, g, beta, S0 = rand_inputs(34, B=1, T=5, state=True, unit=False)
+    q[:, 2] = 0.0
+    k[:, 2] = 0.0
+    o, s = orc.seq(q[:, :3], k[:, :3], v[:, :3], g[:, :3], beta[:, :3], S0, qk_norm=True)
+    _, s2 = orc.seq(q[:, :2], k[:, :2], v[:, :2], g[:, :2], beta[:, :2], S0, qk_norm=True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(s))
+    np.testing.assert_array_equal(o[:, 2], 0.0)
+    a = np.exp(g[0, 2].astype(np.float64))
+    np.testing.assert_allclose(s[0], a[:, None, None] * s2[0], rtol=1e-14, atol=1e-300)
