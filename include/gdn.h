@@ -30,8 +30,8 @@
  *   - q, k, v and o hold elements of type `dtype` (bf16 = 2-byte bfloat16, f32 = float);
  *     g, beta and the state are always float (fp32).
  *   - q, k, v, o, state pointers must be 16-byte aligned; g, beta 4-byte aligned.
- *   - No query scaling is applied and q, k are used as given (callers that want
- *     L2-normalised q, k normalise them first).  g must be finite (a_t > 0).
+ *   - No query scaling is applied.  gdn_prefill and gdn_decode_step use q, k as given;
+ *     their _qknorm variants L2-normalise q and k first.  g must be finite (a_t > 0).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work on
  *     it and return without synchronising; argument errors are reported synchronously,
  *     before anything is enqueued.  Asynchronous kernel faults surface on the stream.
@@ -98,6 +98,19 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
                        int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype dtype,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* gdn_prefill with q and k L2-normalised per token and head inside the kernels: every
+ * q_t and k_t above is replaced by x / sqrt(|x|^2 + 1e-6), computed in fp32 from the stored
+ * elements, so that raw projections need no separate normalisation pass ("Optimizing
+ * on-device inference for Apple Silicon", section "Reduce intermediate and state traffic":
+ * the query/key preparation is fused rather than written out and read back).  The stored
+ * q and k are not modified.  Arguments, workspace (size and segmentation), aliasing rules
+ * and status codes are those of gdn_prefill. */
+gdn_status gdn_prefill_qknorm(const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, const float *state_in, void *o,
+                              float *state_out, int B, int T, int Hk, int Hv, int dk, int dv,
+                              int chunk, gdn_dtype dtype, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
 /* The two stages of gdn_prefill, for callers that schedule them separately (for example
  * to overlap the state-independent stage of one segment with other work, or to time each
  * stage).  Same arguments and rules as gdn_prefill, except that they need the one-pass
@@ -133,6 +146,14 @@ gdn_status gdn_prefill_scan(const void *q, const void *k, const void *v, const f
 gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
                            const float *beta, const float *state_in, float *state_out, void *o,
                            int B, int Hk, int Hv, int dk, int dv, gdn_dtype dtype, void *stream);
+
+/* gdn_decode_step with q and k L2-normalised in registers first (x / sqrt(|x|^2 + 1e-6),
+ * fp32), the decode-side fusion of the same section as gdn_prefill_qknorm.  Arguments and
+ * status codes are those of gdn_decode_step. */
+gdn_status gdn_decode_step_qknorm(const void *q, const void *k, const void *v, const float *g,
+                                  const float *beta, const float *state_in, float *state_out,
+                                  void *o, int B, int Hk, int Hv, int dk, int dv, gdn_dtype dtype,
+                                  void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *gdn_status_string(gdn_status status);

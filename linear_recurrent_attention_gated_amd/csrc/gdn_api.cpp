@@ -41,7 +41,7 @@ Layout layout(int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype
     L.Ut = off;  off = round_up(off + (size_t)B * Hv * Tp * dv * es, 256);
     L.P = off;   off = round_up(off + (size_t)B * Hv * Tp * cp * es, 256);
     L.KT = off;  off = round_up(off + (size_t)B * Hk * N * dk * cp * es, 256);
-    L.gam = off; off = round_up(off + (size_t)B * Hv * Tp * 2 * sizeof(float), 256);
+    L.gam = off; off = round_up(off + (size_t)B * Hv * N * (2 * chunk + 4) * sizeof(float), 256);
     L.total = off;
     return L;
 }
@@ -76,7 +76,8 @@ namespace {
 gdn_status prefill_stages(const void* q, const void* k, const void* v, const float* g,
                           const float* beta, const float* state_in, void* o, float* state_out,
                           int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype dtype,
-                          void* workspace, size_t workspace_bytes, void* stream, int stages) {
+                          void* workspace, size_t workspace_bytes, void* stream, int stages,
+                          int qk_norm) {
     const gdn_status sc = shape_check(B, T, Hk, Hv, dk, dv, chunk, dtype, true);
     if (sc != GDN_OK) return sc;
     if (!state_out) return GDN_ERR_NULL;
@@ -138,6 +139,7 @@ gdn_status prefill_stages(const void* q, const void* k, const void* v, const flo
         p.gam = reinterpret_cast<float*>(ws + L.gam);
         p.B = B; p.T = Tp; p.Hk = Hk; p.Hv = Hv; p.N = (Tp + chunk - 1) / chunk;
         p.Ts = T; p.t0 = t0;
+        p.qk_norm = qk_norm;
 
         hipError_t e = hipErrorInvalidValue;
         if (dtype == GDN_BF16) {
@@ -163,7 +165,16 @@ gdn_status gdn_prefill(const void* q, const void* k, const void* v, const float*
                        int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype dtype,
                        void* workspace, size_t workspace_bytes, void* stream) {
     return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
-                          dtype, workspace, workspace_bytes, stream, 3);
+                          dtype, workspace, workspace_bytes, stream, 3, 0);
+}
+
+gdn_status gdn_prefill_qknorm(const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, const float* state_in, void* o,
+                              float* state_out, int B, int T, int Hk, int Hv, int dk, int dv,
+                              int chunk, gdn_dtype dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
+                          dtype, workspace, workspace_bytes, stream, 3, 1);
 }
 
 gdn_status gdn_prefill_prepare(const void* q, const void* k, const void* v, const float* g,
@@ -172,7 +183,7 @@ gdn_status gdn_prefill_prepare(const void* q, const void* k, const void* v, cons
                                int chunk, gdn_dtype dtype, void* workspace,
                                size_t workspace_bytes, void* stream) {
     return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
-                          dtype, workspace, workspace_bytes, stream, 1);
+                          dtype, workspace, workspace_bytes, stream, 1, 0);
 }
 
 gdn_status gdn_prefill_scan(const void* q, const void* k, const void* v, const float* g,
@@ -181,12 +192,16 @@ gdn_status gdn_prefill_scan(const void* q, const void* k, const void* v, const f
                             gdn_dtype dtype, void* workspace, size_t workspace_bytes,
                             void* stream) {
     return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
-                          dtype, workspace, workspace_bytes, stream, 2);
+                          dtype, workspace, workspace_bytes, stream, 2, 0);
 }
 
-gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const float* g,
-                           const float* beta, const float* state_in, float* state_out, void* o,
-                           int B, int Hk, int Hv, int dk, int dv, gdn_dtype dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+gdn_status decode(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                  const float* state_in, float* state_out, void* o, int B, int Hk, int Hv, int dk,
+                  int dv, gdn_dtype dtype, void* stream, int qk_norm) {
     const gdn_status sc = shape_check(B, 1, Hk, Hv, dk, dv, 16, dtype, false);
     if (sc != GDN_OK) return sc;
     if (!q || !k || !v || !g || !beta || !state_in || !state_out || !o) return GDN_ERR_NULL;
@@ -206,10 +221,27 @@ gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const fl
 
     gdn::DecodeParams p;
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.state_in = state_in;
-    p.state_out = state_out; p.o = o; p.B = B; p.Hk = Hk; p.Hv = Hv;
+    p.state_out = state_out; p.o = o; p.B = B; p.Hk = Hk; p.Hv = Hv; p.qk_norm = qk_norm;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const hipError_t e = dtype == GDN_BF16 ? gdn::decode_bf16(dk, dv, p, st) : gdn::decode_f32(dk, dv, p, st);
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const float* state_in, float* state_out, void* o,
+                           int B, int Hk, int Hv, int dk, int dv, gdn_dtype dtype, void* stream) {
+    return decode(q, k, v, g, beta, state_in, state_out, o, B, Hk, Hv, dk, dv, dtype, stream, 0);
+}
+
+gdn_status gdn_decode_step_qknorm(const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, const float* state_in, float* state_out,
+                                  void* o, int B, int Hk, int Hv, int dk, int dv, gdn_dtype dtype,
+                                  void* stream) {
+    return decode(q, k, v, g, beta, state_in, state_out, o, B, Hk, Hv, dk, dv, dtype, stream, 1);
 }
 
 const char* gdn_status_string(gdn_status s) {

@@ -11,6 +11,8 @@
 //   delta_i = beta (v_i - a s_k)                   a = exp(g)
 //   S_i <- a S_i + delta_i k^T
 //   o_i = S_i(new) . q = a s_q + delta_i (k . q)
+// With fused normalisation q and k are first scaled to unit length (each lane group of a
+// row reduces the squared norm with the same shuffles as the dot products).
 //
 // Mapping: a row of dk floats is read by dk/4 consecutive lanes as 16-byte vectors, so
 // a wavefront reads 1 KiB of contiguous state per instruction; each thread keeps NIT
@@ -32,6 +34,7 @@ struct DecodeParams {
     float* state_out;     // [B][Hv][DV][DK]
     void* o;              // [B][Hv][DV]
     int B, Hk, Hv;
+    int qk_norm;          // nonzero: q and k are L2-normalised per head first
 };
 
 template <typename E, int DK, int DV>
@@ -57,6 +60,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     float kk[4], qq[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) { kk[e] = X::to_f(kp[e]); qq[e] = X::to_f(qp[e]); }
+    if (p.qk_norm) {   // the LPR lanes of a row hold the whole vector between them
+        float ssk = kk[0] * kk[0] + kk[1] * kk[1] + kk[2] * kk[2] + kk[3] * kk[3];
+        float ssq = qq[0] * qq[0] + qq[1] * qq[1] + qq[2] * qq[2] + qq[3] * qq[3];
+#pragma unroll
+        for (int off = LPR / 2; off > 0; off >>= 1) {
+            ssk += __shfl_xor(ssk, off, 64);
+            ssq += __shfl_xor(ssq, off, 64);
+        }
+        const float ik = rsqrtf(ssk + kNormEps), iq = rsqrtf(ssq + kNormEps);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { kk[e] *= ik; qq[e] *= iq; }
+    }
 
     const size_t row0 = ((size_t)b * p.Hv + h) * DV + (size_t)blk * RPB + rloc;
     float4 s[NIT];

@@ -127,6 +127,13 @@ template <> struct Elem<float> {
 
 __device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
 
+// element e of an operand fragment, as stored
+__device__ __forceinline__ bf16_t frag_elem(bf16x8 f, int e) { return __builtin_bit_cast(u16x8, f)[e]; }
+__device__ __forceinline__ float frag_elem(float f, int) { return f; }
+
+// L2 normalisation of q and k, x / sqrt(|x|^2 + eps): eps keeps a zero vector finite
+constexpr float kNormEps = 1e-6f;
+
 // Workgroup barrier for LDS traffic: wait until this wave's LDS reads and writes have
 // completed, then synchronise the waves.  Unlike __syncthreads() it does not wait for
 // outstanding global loads or stores, so prefetches and output stores stay in flight across

@@ -41,8 +41,10 @@
 //   P   [B][Hv][N][C/16][NKC]   fragments   A operand of P U     (rows tokens, k = tokens; permuted)
 //   KT  [B][Hk][N][DK/16][NKC]  fragments   A operand of K^T U'  (rows dk,     k = tokens; permuted)
 //   Ut  [B][Hv][N][DV/16][C/16] accumulator tiles (lane: col l % 16, rows 4 (l/16) + [0,4))
-//   gam [B][Hv][N][2][C] fp32 gate factors per chunk: exp(gamma_r), then exp(gamma_last - gamma_r)
-//       (rows past the end repeat the last row's gamma)
+//   gam [B][Hv][N][2C + 4] fp32 gate factors per chunk: [0, C) the output scale exp(gamma_r),
+//       [C, 2C) the update scale exp(gamma_last - gamma_r), [2C] the chunk decay
+//       exp(gamma_last) (rows past the end repeat the last row's gamma).  With fused q/k
+//       normalisation the output scale also carries 1 / |q_r| and the update scale 1 / |k_r|.
 // NKC = ceil(C / KB); k-values past the chunk are stored as zeros.
 #pragma once
 
@@ -73,6 +75,8 @@ struct PrefillParams {
     // (Ts = the arrays' tokens per batch, t0 = first token of the pass).  A prompt run in
     // several passes carries the state between them through state_out.
     int Ts, t0;
+    // nonzero: q and k are L2-normalised per token and head inside the kernels
+    int qk_norm;
 };
 
 constexpr int kThreads = 256;
@@ -89,6 +93,7 @@ struct PrefillShape {
     static constexpr size_t P_PER_CHUNK = (size_t)NT * NKC * FRAG;
     static constexpr size_t KT_PER_CHUNK = (size_t)(DK / 16) * NKC * FRAG;
     static constexpr size_t UT_PER_CHUNK = (size_t)(DV / 16) * NT * 256;
+    static constexpr int GATES = 2 * C + 4;   // fp32 gate factors per chunk (16-byte multiple)
 };
 
 // Index (tm, tn), tn <= tm, of the tt-th 16x16 tile of a lower-triangular tile grid.
@@ -167,8 +172,10 @@ __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <typename E, int DK, int DV, int C>
-__global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) {
+// NORM: q and k are L2-normalised (p.qk_norm); a separate instantiation, so that the plain
+// path carries none of its registers.
+template <typename E, int DK, int DV, int C, bool NORM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void intra_chunk_kernel(PrefillParams p) {
     using S = PrefillShape<E, DK, DV, C>;
     using X = Elem<E>;
     typedef typename X::frag frag;
@@ -189,6 +196,14 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
     __shared__ __align__(16) float sg2[C];        // gamma * log2(e)
     __shared__ __align__(16) float sbeta[CP];
     __shared__ __align__(16) float sbg[CP];       // beta * Gamma
+    // 1 / |k_r| and 1 / |q_r| of the fused normalisation (NORM only)
+    __shared__ __align__(16) float sinvk[NORM ? CP : 4];
+    __shared__ __align__(16) float sinvq[NORM ? C : 4];
+    auto invk = [&](int r) { return NORM ? sinvk[r] : 1.f; };
+    auto invk4 = [&](int r) {
+        if constexpr (NORM) return *reinterpret_cast<const float4*>(sinvk + r);
+        return make_float4(1.f, 1.f, 1.f, 1.f);
+    };
 
     const int T = p.T, Hk = p.Hk, Hv = p.Hv, N = p.N;
     const int grp = Hv / Hk;
@@ -327,16 +342,66 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
             sbeta[lane] = bt;
             sbg[lane] = bt * exp2f(x2);
         }
-        if (lane < C) {   // gate factors for the scan: exp(gamma_r), exp(gamma_last - gamma_r)
-            float* gf = p.gam + (bh * N + c) * 2 * C;
-            gf[lane] = exp2f(x2);
-            gf[C + lane] = exp2f(gl2 - x2);
+        if constexpr (!NORM) {   // gate factors for the scan (with NORM: below, scaled)
+            float* gf = p.gam + (bh * N + c) * S::GATES;
+            if (lane < C) {
+                gf[lane] = exp2f(x2);
+                gf[C + lane] = exp2f(gl2 - x2);
+            }
+            if (lane == 0) gf[2 * C] = exp2f(gl2);
         }
     }
     load_kvg(nxt);   // registers consumed above; the next item's rows are in flight from here
 #pragma unroll
     for (int kb = 0; kb < NKD; ++kb) qf[kb] = X::keep_if(qf[kb], pm_ld * 16 + rl < n);
     lds_barrier();   // (B1)
+    if constexpr (NORM) {
+        // 1 / |k_r| from the K rows in LDS (four threads per row), 1 / |q_r| from each wave's
+        // Q row tile (lane groups hold a quarter of a row each); rows past the chunk are zero
+        constexpr int QPR = DK / 4;
+        if (tid < 4 * C) {
+            const int r = tid / 4, part = tid % 4;
+            float ss = 0.f;
+#pragma unroll
+            for (int v = 0; v < QPR / EPV; ++v) {
+                const uint4 u = *reinterpret_cast<const uint4*>(Ks + r * LDK + part * QPR + v * EPV);
+                const E* e = reinterpret_cast<const E*>(&u);
+#pragma unroll
+                for (int j = 0; j < EPV; ++j) {
+                    const float x = X::to_f(e[j]);
+                    ss += x * x;
+                }
+            }
+            ss += __shfl_xor(ss, 1, 64);
+            ss += __shfl_xor(ss, 2, 64);
+            if (part == 0) sinvk[r] = rsqrtf(ss + kNormEps);
+        }
+        if (tid < CP - C) sinvk[C + tid] = 1.f;
+        if (has_prow) {
+            float ss = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < NKD; ++kb)
+#pragma unroll
+                for (int e = 0; e < KPL; ++e) {
+                    const float x = X::to_f(frag_elem(qf[kb], e));
+                    ss += x * x;
+                }
+            ss += __shfl_xor(ss, 16, 64);
+            ss += __shfl_xor(ss, 32, 64);
+            if (g == 0) sinvq[pm * 16 + rl] = rsqrtf(ss + kNormEps);
+        }
+        lds_barrier();
+        if (wave == 0) {
+            float* gf = p.gam + (bh * N + c) * S::GATES;
+            const float gl2 = sg2[C - 1];
+            if (lane < C) {
+                const float x2 = sg2[lane];
+                gf[lane] = exp2f(x2) * sinvq[lane];
+                gf[C + lane] = exp2f(gl2 - x2) * sinvk[lane];
+            }
+            if (lane == 0) gf[2 * C] = exp2f(gl2);
+        }
+    }
 
     // Gram tile of K rows: D[r][s] = k_r . k_s  (r in tile tm, s in tile tn)
     auto kk_tile = [&](int tm, int tn) {
@@ -350,14 +415,15 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
     // A[r][s] = beta_r exp(gamma_r - gamma_s) (k_r . k_s) for s < r, from a Gram tile
     auto mask_a = [&](int tm, int tn, f32x4 G) {
         const int s = tn * 16 + rl;
-        const float gs = sg2[s];
+        const float gs = sg2[s], ks = invk(s);
         const float4 gr = *reinterpret_cast<const float4*>(sg2 + tm * 16 + rq);
         const float4 br = *reinterpret_cast<const float4*>(sbeta + tm * 16 + rq);
-        const float grv[4] = {gr.x, gr.y, gr.z, gr.w}, brv[4] = {br.x, br.y, br.z, br.w};
+        const float4 kr4 = invk4(tm * 16 + rq);
+        const float grv[4] = {gr.x, gr.y, gr.z, gr.w}, brv[4] = {br.x * kr4.x, br.y * kr4.y, br.z * kr4.z, br.w * kr4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = tm * 16 + rq + j;
-            sR[r * LDR + s] = (s < r) ? brv[j] * fast_exp2(grv[j] - gs) * G[j] : 0.f;
+            sR[r * LDR + s] = (s < r) ? brv[j] * ks * fast_exp2(grv[j] - gs) * G[j] : 0.f;
         }
     };
     // P row tile m: P[r][s] = exp(gamma_r - gamma_s) (q_r . k_s), s <= r, stored as permuted
@@ -365,7 +431,7 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
     auto p_row = [&](int m) {
         E* Pg = reinterpret_cast<E*>(p.P) + (bh * N + c) * S::P_PER_CHUNK;
         const int r = m * 16 + rl;
-        const float gr = sg2[r];
+        const float gr = sg2[r], qs = NORM ? sinvq[r] : 1.f;
         auto ptile = [&](int t) {
             f32x4 acc = zero4();
             if (t <= m) {
@@ -373,11 +439,12 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
 #pragma unroll
                 for (int kb = 0; kb < NKD; ++kb) acc = X::mma(X::ld(ar + kb * KB), qf[kb], acc);
                 const float4 gs = *reinterpret_cast<const float4*>(sg2 + t * 16 + rq);
-                const float gsv[4] = {gs.x, gs.y, gs.z, gs.w};
+                const float4 ks = invk4(t * 16 + rq);
+                const float gsv[4] = {gs.x, gs.y, gs.z, gs.w}, ksv[4] = {ks.x, ks.y, ks.z, ks.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int s = t * 16 + rq + j;
-                    acc[j] = (s <= r) ? fast_exp2(gr - gsv[j]) * acc[j] : 0.f;
+                    acc[j] = (s <= r) ? qs * ksv[j] * fast_exp2(gr - gsv[j]) * acc[j] : 0.f;
                 }
             }
             return acc;
@@ -529,7 +596,7 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(PrefillParams p) 
 #pragma unroll
                 for (int e = 0; e < KPL; ++e) {
                     const float rv = rrow[kb * KB + e];
-                    aw[e] = rv * sbg[kb * KB + kq + e];
+                    aw[e] = rv * sbg[kb * KB + kq + e] * invk(kb * KB + kq + e);
                     au[e] = rv * sbeta[kb * KB + kq + e];
                 }
                 rw[kb] = X::ld_f(aw);
@@ -605,8 +672,8 @@ struct ChainOperands {
     frag w[NKD];
     frag kt[TPW][NKC];
     E ut[4];
-    f32x4 e;      // exp(gamma_last - gamma_r) for this lane's four token rows
-    float gn;     // exp(gamma_last)
+    f32x4 e;      // update scale of this lane's four token rows
+    float gn;     // chunk decay exp(gamma_last)
 };
 
 template <typename E, int DK, int C>
@@ -617,7 +684,7 @@ struct OutputOperands {
     static constexpr int NKC = (C + X::KB - 1) / X::KB;
     frag q[NKD];
     frag p[NKC];
-    f32x4 gr;     // exp(gamma_r) for this lane's four token rows
+    f32x4 gr;     // output scale of this lane's four token rows
 };
 
 template <typename E, int DK, int DV, int C, bool SPLIT>
@@ -666,7 +733,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
     std::integral_constant<bool, false> full;
     std::integral_constant<bool, true> tail;
 
-    const float* gates = p.gam + (size_t)bh * N * 2 * C;   // per chunk: exp(gamma) then exp(gl - gamma)
+    const float* gates = p.gam + (size_t)bh * N * Sh::GATES;   // per chunk: see the workspace layout
 
     for (int e = tid; e < 16 * LDU; e += kScanThreads) {   // columns past the chunk read as zero
         UT[e] = X::from_f(0.f);
@@ -679,8 +746,8 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
         const E* KTg = reinterpret_cast<const E*>(p.KT) + ((size_t)b * Hk + hk) * N * Sh::KT_PER_CHUNK;
 
         auto fetch = [&](COps& op, int c) {
-            const float* gc = gates + (size_t)c * 2 * C;
-            op.gn = gc[C - 1];
+            const float* gc = gates + (size_t)c * Sh::GATES;
+            op.gn = gc[2 * C];
             op.e = *reinterpret_cast<const f32x4*>(gc + C + m * 16 + rq);
             const E* wsrc = Wg + (size_t)c * Sh::W_PER_CHUNK + (size_t)m * NKD * Sh::FRAG + lane * KPL;
 #pragma unroll
@@ -805,7 +872,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
 
         auto fetch = [&](OOps& op, int c) {
             const int t0 = c * C;
-            op.gr = *reinterpret_cast<const f32x4*>(gates + (size_t)c * 2 * C + m * 16 + rq);
+            op.gr = *reinterpret_cast<const f32x4*>(gates + (size_t)c * Sh::GATES + m * 16 + rq);
             const int tq = t0 + m * 16 + rl;
             const E* qsrc = qg + ((size_t)b * p.Ts + p.t0 + min(tq, T - 1)) * Hk * DK + kq;
 #pragma unroll
@@ -868,7 +935,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
 
 // Workgroups of the intra kernel that fit on the current device at once (the kernel loops
 // over its work items, so it is launched with exactly that many), cached per device.
-template <typename E, int DK, int DV, int C>
+template <typename E, int DK, int DV, int C, bool NORM>
 inline int intra_capacity() {
     static std::atomic<int> cache[64];
     int dev = 0;
@@ -877,7 +944,7 @@ inline int intra_capacity() {
     if (cap == 0) {
         int ncu = 0, per = 0;
         if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) ncu = 1;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, intra_chunk_kernel<E, DK, DV, C>, kThreads, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, intra_chunk_kernel<E, DK, DV, C, NORM>, kThreads, 0) !=
             hipSuccess)
             per = 1;
         cap = std::max(1, ncu) * std::max(1, per);
@@ -894,8 +961,14 @@ inline hipError_t launch_prefill(const PrefillParams& p, int stages, hipStream_t
         // resident capacity and at most the number of work items
         const int unit = 8 * (p.Hv / p.Hk);
         const int nitems = (p.B * p.N * p.Hk + 7) / 8 * 8 * (p.Hv / p.Hk);
-        const int grid = std::min(nitems, std::max(unit, intra_capacity<E, DK, DV, C>() / unit * unit));
-        intra_chunk_kernel<E, DK, DV, C><<<grid, kThreads, 0, stream>>>(p);
+        auto go = [&](auto norm) {
+            constexpr bool NORM = decltype(norm)::value;
+            const int cap = intra_capacity<E, DK, DV, C, NORM>();
+            const int grid = std::min(nitems, std::max(unit, cap / unit * unit));
+            intra_chunk_kernel<E, DK, DV, C, NORM><<<grid, kThreads, 0, stream>>>(p);
+        };
+        if (p.qk_norm) go(std::true_type{});
+        else go(std::false_type{});
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -18,8 +18,9 @@ GDN_BF16 = 0
 GDN_F32 = 1
 _STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
            4: "GDN_ERR_ALIGN", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP"}
-EXPORTS = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_prepare", "gdn_prefill_scan",
-           "gdn_decode_step", "gdn_status_string", "gdn_abi_version")
+EXPORTS = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_qknorm", "gdn_prefill_prepare",
+           "gdn_prefill_scan", "gdn_decode_step", "gdn_decode_step_qknorm", "gdn_status_string",
+           "gdn_abi_version")
 
 
 class GdnError(RuntimeError):
@@ -42,11 +43,12 @@ def lib():
         P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
         L.gdn_prefill_workspace_bytes.argtypes = [I] * 8
         L.gdn_prefill_workspace_bytes.restype = Z
-        for fn in ("gdn_prefill", "gdn_prefill_prepare", "gdn_prefill_scan"):
+        for fn in ("gdn_prefill", "gdn_prefill_qknorm", "gdn_prefill_prepare", "gdn_prefill_scan"):
             getattr(L, fn).argtypes = [P] * 8 + [I] * 8 + [P, Z, P]
             getattr(L, fn).restype = I
-        L.gdn_decode_step.argtypes = [P] * 8 + [I] * 6 + [P]
-        L.gdn_decode_step.restype = I
+        for fn in ("gdn_decode_step", "gdn_decode_step_qknorm"):
+            getattr(L, fn).argtypes = [P] * 8 + [I] * 6 + [P]
+            getattr(L, fn).restype = I
         L.gdn_status_string.argtypes = [I]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
@@ -108,6 +110,12 @@ def gdn_prefill(q, k, v, g, beta, state_in, o, state_out, chunk, workspace, stre
                   stream)
 
 
+def gdn_prefill_qknorm(q, k, v, g, beta, state_in, o, state_out, chunk, workspace, stream=None):
+    """Calls gdn_prefill_qknorm (q and k L2-normalised inside); arguments as gdn_prefill."""
+    _prefill_call("gdn_prefill_qknorm", q, k, v, g, beta, state_in, o, state_out, chunk,
+                  workspace, stream)
+
+
 def gdn_prefill_prepare(q, k, v, g, beta, state_in, o, state_out, chunk, workspace, stream=None):
     """Calls gdn_prefill_prepare (the state-independent stage); arguments as gdn_prefill."""
     _prefill_call("gdn_prefill_prepare", q, k, v, g, beta, state_in, o, state_out, chunk,
@@ -145,6 +153,16 @@ def _prefill_call(fn, q, k, v, g, beta, state_in, o, state_out, chunk, workspace
 def gdn_decode_step(q, k, v, g, beta, state_in, state_out, o, stream=None):
     """Calls gdn_decode_step.  q, k [B,Hk,dk]; v, o [B,Hv,dv]; g, beta [B,Hv] fp32;
     state_in / state_out [B,Hv,dv,dk] fp32 (may be the same tensor)."""
+    _decode_call("gdn_decode_step", q, k, v, g, beta, state_in, state_out, o, stream)
+
+
+def gdn_decode_step_qknorm(q, k, v, g, beta, state_in, state_out, o, stream=None):
+    """Calls gdn_decode_step_qknorm (q and k L2-normalised inside); arguments as
+    gdn_decode_step."""
+    _decode_call("gdn_decode_step_qknorm", q, k, v, g, beta, state_in, state_out, o, stream)
+
+
+def _decode_call(fn, q, k, v, g, beta, state_in, state_out, o, stream):
     B, Hk, dk = q.shape
     Hv, dv = v.shape[1], v.shape[2]
     dt = _dt(q)
@@ -157,16 +175,17 @@ def gdn_decode_step(q, k, v, g, beta, state_in, state_out, o, stream=None):
             tuple(g.shape) != (B, Hv) or tuple(beta.shape) != (B, Hv) or \
             tuple(state_in.shape) != (B, Hv, dv, dk) or tuple(state_out.shape) != (B, Hv, dv, dk):
         raise ValueError("inconsistent shapes")
-    rc = lib().gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
-                               _ptr(state_out), _ptr(o), B, Hk, Hv, dk, dv, dt, _stream(stream))
+    rc = getattr(lib(), fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+                            _ptr(state_out), _ptr(o), B, Hk, Hv, dk, dv, dt, _stream(stream))
     if rc != 0:
-        raise GdnError("gdn_decode_step", rc)
+        raise GdnError(fn, rc)
 
 
 # -- conveniences that allocate outputs with torch --------------------------------------------
 
-def prefill(q, k, v, g, beta, state=None, chunk=64, workspace=None, stream=None):
-    """Returns (o, state_out); allocates o, state_out and (if not given) the workspace."""
+def prefill(q, k, v, g, beta, state=None, chunk=64, workspace=None, stream=None, qk_norm=False):
+    """Returns (o, state_out); allocates o, state_out and (if not given) the workspace.
+    qk_norm: L2-normalise q and k inside the kernels (gdn_prefill_qknorm)."""
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
     o = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=q.device)
@@ -174,12 +193,15 @@ def prefill(q, k, v, g, beta, state=None, chunk=64, workspace=None, stream=None)
     if workspace is None and T > 0:
         nb = gdn_prefill_workspace_bytes(B, T, Hk, Hv, dk, dv, chunk, q.dtype)
         workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
-    gdn_prefill(q, k, v, g, beta, state, o, s_out, chunk, workspace, stream)
+    (gdn_prefill_qknorm if qk_norm else gdn_prefill)(q, k, v, g, beta, state, o, s_out, chunk,
+                                                     workspace, stream)
     return o, s_out
 
 
-def decode_step(q, k, v, g, beta, state, stream=None):
-    """Updates ``state`` in place and returns o [B,Hv,dv]."""
+def decode_step(q, k, v, g, beta, state, stream=None, qk_norm=False):
+    """Updates ``state`` in place and returns o [B,Hv,dv].  qk_norm: L2-normalise q and k
+    inside the kernel (gdn_decode_step_qknorm)."""
     o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
-    gdn_decode_step(q, k, v, g, beta, state, state, o, stream)
+    (gdn_decode_step_qknorm if qk_norm else gdn_decode_step)(q, k, v, g, beta, state, state, o,
+                                                             stream)
     return o

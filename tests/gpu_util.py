@@ -31,10 +31,10 @@ def np32(t):
     return t.detach().float().cpu().numpy()
 
 
-def oracle_prefill(d, state_in=None, pairs=None, nthreads=None):
+def oracle_prefill(d, state_in=None, pairs=None, nthreads=None, qk_norm=False):
     s = None if state_in is None else np.asarray(state_in, dtype=np.float64)
     return orc.seq(np32(d["q"]), np32(d["k"]), np32(d["v"]), np32(d["g"]), np32(d["beta"]), s,
-                   pairs=pairs, nthreads=nthreads, rows_per_item=8)
+                   pairs=pairs, nthreads=nthreads, rows_per_item=8, qk_norm=qk_norm)
 
 
 def to_dev(d, device="cuda:0"):

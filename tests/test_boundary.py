@@ -38,8 +38,9 @@ def test_abi_version_and_status_strings():
 
 def test_workspace_bytes():
     # prefill at T=4096, Hk=16, Hv=32, dk=dv=128, chunk 64, bf16:
-    # W, Ut: 32*4096*128*2 each; P: 32*4096*64*2; K^T: 16*4096*128*2; gate factors: 32*4096*2*4
-    expect = 2 * 32 * 4096 * 128 * 2 + 32 * 4096 * 64 * 2 + 16 * 4096 * 128 * 2 + 32 * 4096 * 8
+    # W, Ut: 32*4096*128*2 each; P: 32*4096*64*2; K^T: 16*4096*128*2;
+    # gate factors: 32 heads * 64 chunks * (2*64 + 4) floats
+    expect = 2 * 32 * 4096 * 128 * 2 + 32 * 4096 * 64 * 2 + 16 * 4096 * 128 * 2 + 32 * 64 * 132 * 4
     assert gdn.gdn_prefill_workspace_bytes(1, 4096, 16, 32, 128, 128, 64, 0) == expect
     assert gdn.gdn_prefill_workspace_bytes(1, 0, 16, 32, 128, 128, 64, 0) == 0
     assert gdn.gdn_prefill_workspace_bytes(1, 64, 16, 32, 96, 128, 64, 0) == 0     # unsupported
@@ -66,14 +67,14 @@ def _prefill(fn="gdn_prefill", **kw):
                                  a["chunk"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
 
 
-def _decode(**kw):
+def _decode(fn="gdn_decode_step", **kw):
     a = dict(q=BASE, k=BASE + MB, v=BASE + 2 * MB, g=BASE + 3 * MB, beta=BASE + 4 * MB,
              state_in=BASE + 10 * MB, state_out=BASE + 10 * MB, o=BASE + 30 * MB, B=1, Hk=2, Hv=4,
              dk=32, dv=32, dtype=0, stream=None)
     a.update(kw)
-    return gdn.lib().gdn_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state_in"],
-                                     a["state_out"], a["o"], a["B"], a["Hk"], a["Hv"], a["dk"],
-                                     a["dv"], a["dtype"], a["stream"])
+    return getattr(gdn.lib(), fn)(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state_in"],
+                                  a["state_out"], a["o"], a["B"], a["Hk"], a["Hv"], a["dk"],
+                                  a["dv"], a["dtype"], a["stream"])
 
 
 # Each case breaks exactly one rule; the rest of the call is valid.
@@ -91,7 +92,8 @@ PREFILL_ERRORS = [
 ]
 
 
-@pytest.mark.parametrize("fn", ["gdn_prefill", "gdn_prefill_prepare", "gdn_prefill_scan"])
+@pytest.mark.parametrize("fn", ["gdn_prefill", "gdn_prefill_qknorm", "gdn_prefill_prepare",
+                                "gdn_prefill_scan"])
 @pytest.mark.parametrize("kw,code", PREFILL_ERRORS)
 def test_prefill_rejects(kw, code, fn):
     assert _prefill(fn=fn, **kw) == code
@@ -108,9 +110,10 @@ DECODE_ERRORS = [
 ]
 
 
+@pytest.mark.parametrize("fn", ["gdn_decode_step", "gdn_decode_step_qknorm"])
 @pytest.mark.parametrize("kw,code", DECODE_ERRORS)
-def test_decode_rejects(kw, code):
-    assert _decode(**kw) == code
+def test_decode_rejects(kw, code, fn):
+    assert _decode(fn=fn, **kw) == code
 
 
 def test_python_binding_raises_with_status():
