@@ -37,6 +37,32 @@ struct DecodeParams {
     int qk_norm;          // nonzero: q and k are L2-normalised per head first
 };
 
+// Sum over each aligned group of L lanes (L = 8, 16 or 32), returned to every lane of the
+// group: two quad permutations, the half-row and row mirrors (DPP, on the VALU), and for 32
+// the gfx950 row swap.  Every lane adds the same two partial sums (in either order), so all
+// lanes of a group hold the bitwise-same result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+template <int L>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(L == 8 || L == 16 || L == 32, "group size");
+    x += dpp_f<0xB1>(x);    // quad_perm [1,0,3,2]: partner lane ^ 1
+    x += dpp_f<0x4E>(x);    // quad_perm [2,3,0,1]: partner lane ^ 2
+    x += dpp_f<0x141>(x);   // row_half_mirror: the other quad of each 8 lanes
+    if constexpr (L >= 16) x += dpp_f<0x140>(x);   // row_mirror: the other half of each 16
+    if constexpr (L >= 32) {
+        // swap odd rows of one copy with even rows of the other: the pair of results holds,
+        // in every lane, its own row's value and its partner row's (rows of 16 lanes)
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                        false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    return x;
+}
+
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     using X = Elem<E>;
@@ -55,50 +81,45 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     const int sub = tid % LPR, rloc = tid / LPR;
     const int c0 = sub * 4;
 
-    const E* kp = reinterpret_cast<const E*>(p.k) + ((size_t)b * p.Hk + hk) * DK + c0;
-    const E* qp = reinterpret_cast<const E*>(p.q) + ((size_t)b * p.Hk + hk) * DK + c0;
-    float kk[4], qq[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { kk[e] = X::to_f(kp[e]); qq[e] = X::to_f(qp[e]); }
-    if (p.qk_norm) {   // the LPR lanes of a row hold the whole vector between them
-        float ssk = kk[0] * kk[0] + kk[1] * kk[1] + kk[2] * kk[2] + kk[3] * kk[3];
-        float ssq = qq[0] * qq[0] + qq[1] * qq[1] + qq[2] * qq[2] + qq[3] * qq[3];
-#pragma unroll
-        for (int off = LPR / 2; off > 0; off >>= 1) {
-            ssk += __shfl_xor(ssk, off, 64);
-            ssq += __shfl_xor(ssq, off, 64);
-        }
-        const float ik = rsqrtf(ssk + kNormEps), iq = rsqrtf(ssq + kNormEps);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { kk[e] *= ik; qq[e] *= iq; }
-    }
-
+    // Every global load is issued before the first use, so the whole step costs one memory
+    // round trip: the state rows, this thread's v elements, q, k, g and beta.
     const size_t row0 = ((size_t)b * p.Hv + h) * DV + (size_t)blk * RPB + rloc;
     float4 s[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it)
         s[it] = *reinterpret_cast<const float4*>(p.state_in + (row0 + (size_t)it * RIT) * DK + c0);
-
-    const float a = expf(p.g[(size_t)b * p.Hv + h]);
-    const float bt = p.beta[(size_t)b * p.Hv + h];
-    float kq = kk[0] * qq[0] + kk[1] * qq[1] + kk[2] * qq[2] + kk[3] * qq[3];
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) kq += __shfl_xor(kq, off, 64);
-
     const E* vp = reinterpret_cast<const E*>(p.v);
+    E vr[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) vr[it] = vp[row0 + (size_t)it * RIT];
+    const E* kp = reinterpret_cast<const E*>(p.k) + ((size_t)b * p.Hk + hk) * DK + c0;
+    const E* qp = reinterpret_cast<const E*>(p.q) + ((size_t)b * p.Hk + hk) * DK + c0;
+    E kraw[4], qraw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { kraw[e] = kp[e]; qraw[e] = qp[e]; }
+    const float graw = p.g[(size_t)b * p.Hv + h];
+    const float bt = p.beta[(size_t)b * p.Hv + h];
+
+    float kk[4], qq[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { kk[e] = X::to_f(kraw[e]); qq[e] = X::to_f(qraw[e]); }
+    if (p.qk_norm) {   // the LPR lanes of a row hold the whole vector between them
+        const float ssk = group_sum<LPR>(kk[0] * kk[0] + kk[1] * kk[1] + kk[2] * kk[2] + kk[3] * kk[3]);
+        const float ssq = group_sum<LPR>(qq[0] * qq[0] + qq[1] * qq[1] + qq[2] * qq[2] + qq[3] * qq[3]);
+        const float ik = rsqrtf(ssk + kNormEps), iq = rsqrtf(ssq + kNormEps);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { kk[e] *= ik; qq[e] *= iq; }
+    }
+    const float a = expf(graw);
+    const float kq = group_sum<LPR>(kk[0] * qq[0] + kk[1] * qq[1] + kk[2] * qq[2] + kk[3] * qq[3]);
+
     E* op = reinterpret_cast<E*>(p.o);
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-        float sk = s[it].x * kk[0] + s[it].y * kk[1] + s[it].z * kk[2] + s[it].w * kk[3];
-        float sq = s[it].x * qq[0] + s[it].y * qq[1] + s[it].z * qq[2] + s[it].w * qq[3];
-#pragma unroll
-        for (int off = LPR / 2; off > 0; off >>= 1) {
-            sk += __shfl_xor(sk, off, 64);
-            sq += __shfl_xor(sq, off, 64);
-        }
+        const float sk = group_sum<LPR>(s[it].x * kk[0] + s[it].y * kk[1] + s[it].z * kk[2] + s[it].w * kk[3]);
+        const float sq = group_sum<LPR>(s[it].x * qq[0] + s[it].y * qq[1] + s[it].z * qq[2] + s[it].w * qq[3]);
         const size_t row = row0 + (size_t)it * RIT;
-        const float vi = X::to_f(vp[row]);
-        const float delta = bt * (vi - a * sk);
+        const float delta = bt * (X::to_f(vr[it]) - a * sk);
         float4 ns;
         ns.x = a * s[it].x + delta * kk[0];
         ns.y = a * s[it].y + delta * kk[1];
