@@ -48,8 +48,8 @@ PREFILL_FLOP_PER_TOKEN_HEAD = 2 * (64 * 128 + 64 * 128 + 2 * 64 * 128 + 3 * 128 
 DECODE_BYTES_PER_LAYER = 2 * STATE_BYTES + PREFILL_BYTES_PER_TOKEN                  # 4,219,136
 
 SOURCES = ["linear_recurrent_attention_gated_amd/csrc/" + f for f in
-           ("gdn_device.h", "gdn_prefill.h", "gdn_decode.h", "gdn_launch.h", "gdn_api.cpp",
-            "gdn_prefill_inst.hip", "gdn_decode.hip")]
+           ("gdn_device.h", "gdn_prefill.h", "gdn_decode.h", "gdn_sequential.h", "gdn_launch.h",
+            "gdn_api.cpp", "gdn_prefill_inst.hip", "gdn_decode.hip", "gdn_sequential.hip")]
 
 
 def kernel_source_hash():
@@ -154,13 +154,71 @@ def parse():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script "
                          "with --copy-calibration into profiles/hbm_traffic.txt, then exit")
+    ap.add_argument("--crossover", action="store_true",
+                    help="time the token-sequential and the blockwise prefill on prefixes of the "
+                         "128K long-memory draw (cold, 16/32 heads, d=128, bf16), print one JSON "
+                         "line, then exit")
     return ap.parse_args()
+
+
+CROSSOVER_T = (1, 8, 16, 32, 64, 96, 128, 192, 256, 512, 1024, 4096, 16384, 131072)
+
+
+def crossover(args):
+    """Both prefill forms on prefixes of one draw, each call cold (the flush fill first)."""
+    import numpy as np
+    import torch
+
+    from linear_recurrent_attention_gated_amd import gdn
+    from linear_recurrent_attention_gated_amd.inputs import LONG_128K, workload_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = LONG_128K
+    host = workload_inputs(w, torch.bfloat16)
+    full = {k: host[k].to(dev) for k in ("q", "k", "v", "g", "beta")}
+    del host
+    Hk, Hv, dk, dv, C = w.Hk, w.Hv, w.dk, w.dv, w.chunk
+    ws = torch.empty(gdn.gdn_prefill_workspace_bytes(1, max(CROSSOVER_T), Hk, Hv, dk, dv, C,
+                                                     torch.bfloat16), dtype=torch.uint8, device=dev)
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    s_out = torch.empty((1, Hv, dv, dk), dtype=torch.float32, device=dev)
+    points = []
+    for T in CROSSOVER_T:
+        d = {k: v[:, :T].contiguous() for k, v in full.items()}
+        o = torch.empty((1, T, Hv, dv), dtype=torch.bfloat16, device=dev)
+        res = {"T": T}
+        for name, flags in (("sequential", gdn.GDN_PATH_SEQUENTIAL), ("blockwise", 0)):
+            reps = 5 if T <= 16384 else 2
+            ts = []
+            for r in range(reps + 1):
+                scratch.fill_(r & 0xFF)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                gdn.gdn_prefill_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], None, o, s_out, C, ws,
+                                   flags)
+                e1.record()
+                torch.cuda.synchronize()
+                if r:
+                    ts.append(e0.elapsed_time(e1) * 1e3)
+            res[name + "_us"] = round(float(np.median(ts)), 2)
+        points.append(res)
+        print("[crossover]", res, file=sys.stderr, flush=True)
+    faster = [p["T"] for p in points if p["sequential_us"] < p["blockwise_us"]]
+    print(json.dumps({"crossover": {
+        "workload": w.name + " prefixes, zero start state, cold", "points": points,
+        "sequential_faster_at": faster,
+        "auto_max_tokens": gdn.gdn_prefill_sequential_max_tokens(1, Hk, Hv, dk, dv,
+                                                                 torch.bfloat16)}}), flush=True)
 
 
 def main():
     args = parse()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return
+    if args.crossover:
+        crossover(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the gated-delta-rule core is built and measured "

@@ -111,6 +111,36 @@ gdn_status gdn_prefill_qknorm(const void *q, const void *k, const void *v, const
                               int chunk, gdn_dtype dtype, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/* Flags of gdn_prefill_ex (bitwise or). */
+#define GDN_QK_NORM 1u         /* L2-normalise q and k inside, as gdn_prefill_qknorm         */
+#define GDN_PATH_SEQUENTIAL 2u /* token-sequential scan, state in registers (see below)     */
+#define GDN_PATH_AUTO 4u       /* sequential when T <= gdn_prefill_sequential_max_tokens(),
+                                  blockwise otherwise                                        */
+
+/* Prefill with a choice of evaluation form ("Optimizing on-device inference for Apple
+ * Silicon", section "Qwen creates three distinct workload shapes": the tokens can be scanned
+ * directly while carrying the state, or the updates regrouped into blocks; which is faster
+ * depends on the dimensions, the workload and the hardware).
+ *   flags without a path bit: the blockwise form, exactly gdn_prefill (or gdn_prefill_qknorm
+ *     with GDN_QK_NORM).
+ *   GDN_PATH_SEQUENTIAL: the form of section "Keep the recurrent state on chip" -- each
+ *     state row split over a few lanes, held in registers for all T tokens, reduced across
+ *     lanes per token, written once at the end; one launch, fp32 throughout.  The workspace
+ *     is not used (it may be NULL; when given it still takes part in the overlap checks).
+ *   GDN_PATH_AUTO: the sequential form for T <= gdn_prefill_sequential_max_tokens(...),
+ *     else the blockwise form.
+ * Arguments, aliasing rules and status codes as gdn_prefill; chunk is validated whatever
+ * the path.  GDN_ERR_UNSUPPORTED for unknown flag bits or both path bits. */
+gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *state_in, void *o, float *state_out,
+                          int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                          gdn_dtype dtype, void *workspace, size_t workspace_bytes, void *stream,
+                          unsigned flags);
+
+/* Longest prompt for which GDN_PATH_AUTO picks the sequential form at these sizes (the
+ * crossover of the two forms measured on MI355X). */
+int gdn_prefill_sequential_max_tokens(int B, int Hk, int Hv, int dk, int dv, gdn_dtype dtype);
+
 /* The two stages of gdn_prefill, for callers that schedule them separately (for example
  * to overlap the state-independent stage of one segment with other work, or to time each
  * stage).  Same arguments and rules as gdn_prefill, except that they need the one-pass

@@ -21,7 +21,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-Wall",
           "-Wno-unused-function", "-I" + CSRC, "-I" + os.path.join(ROOT, "include")]
 
-HEADERS = ["gdn_device.h", "gdn_prefill.h", "gdn_decode.h", "gdn_launch.h"]
+HEADERS = ["gdn_device.h", "gdn_prefill.h", "gdn_decode.h", "gdn_sequential.h", "gdn_launch.h"]
 
 
 def _units():
@@ -31,6 +31,7 @@ def _units():
             tag = f"prefill_{'bf16' if bf else 'f32'}_c{c}"
             units.append((tag, "gdn_prefill_inst.hip", [f"-DGDN_ELEM_BF16={bf}", f"-DGDN_CHUNK={c}"]))
     units.append(("decode", "gdn_decode.hip", []))
+    units.append(("sequential", "gdn_sequential.hip", []))
     units.append(("api", "gdn_api.cpp", []))
     return units
 

@@ -25,6 +25,10 @@ bool overlap(Span a, Span b) {
 }
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Longest prompt for which GDN_PATH_AUTO takes the token-sequential path: measured crossover
+// of the two prefill forms on MI355X at 16 key / 32 value heads, dk = dv = 128, bf16.
+constexpr int kSequentialMaxTokens = 56;
+
 // Workspace regions of the blockwise prefill (see gdn_prefill.h).
 struct Layout {
     size_t W, Ut, P, KT, gam, total;
@@ -77,7 +81,7 @@ gdn_status prefill_stages(const void* q, const void* k, const void* v, const flo
                           const float* beta, const float* state_in, void* o, float* state_out,
                           int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype dtype,
                           void* workspace, size_t workspace_bytes, void* stream, int stages,
-                          int qk_norm) {
+                          int qk_norm, bool sequential) {
     const gdn_status sc = shape_check(B, T, Hk, Hv, dk, dv, chunk, dtype, true);
     if (sc != GDN_OK) return sc;
     if (!state_out) return GDN_ERR_NULL;
@@ -108,6 +112,15 @@ gdn_status prefill_stages(const void* q, const void* k, const void* v, const flo
         if (!(stages & 2)) return GDN_OK;
         return gdn::copy_state(state_in, state_out, (size_t)B * Hv * dv * dk, st) == hipSuccess
                    ? GDN_OK : GDN_ERR_HIP;
+    }
+    if (sequential) {   // the state stays in registers: no workspace, one launch
+        gdn::PrefillParams p{};
+        p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.state_in = state_in;
+        p.o = o; p.state_out = state_out;
+        p.B = B; p.T = T; p.Hk = Hk; p.Hv = Hv; p.N = 0; p.Ts = T; p.t0 = 0; p.qk_norm = qk_norm;
+        const hipError_t e = dtype == GDN_BF16 ? gdn::sequential_bf16(dk, dv, p, st)
+                                               : gdn::sequential_f32(dk, dv, p, st);
+        return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
     }
     if (!workspace) return GDN_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
@@ -165,7 +178,27 @@ gdn_status gdn_prefill(const void* q, const void* k, const void* v, const float*
                        int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype dtype,
                        void* workspace, size_t workspace_bytes, void* stream) {
     return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
-                          dtype, workspace, workspace_bytes, stream, 3, 0);
+                          dtype, workspace, workspace_bytes, stream, 3, 0, false);
+}
+
+gdn_status gdn_prefill_ex(const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const float* state_in, void* o, float* state_out,
+                          int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                          gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream,
+                          unsigned flags) {
+    if (flags & ~(unsigned)(GDN_QK_NORM | GDN_PATH_SEQUENTIAL | GDN_PATH_AUTO) ||
+        ((flags & GDN_PATH_SEQUENTIAL) && (flags & GDN_PATH_AUTO)))
+        return GDN_ERR_UNSUPPORTED;
+    bool seq = (flags & GDN_PATH_SEQUENTIAL) != 0;
+    if (flags & GDN_PATH_AUTO) seq = T <= gdn_prefill_sequential_max_tokens(B, Hk, Hv, dk, dv, dtype);
+    return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
+                          dtype, workspace, workspace_bytes, stream, 3,
+                          (flags & GDN_QK_NORM) ? 1 : 0, seq);
+}
+
+int gdn_prefill_sequential_max_tokens(int B, int Hk, int Hv, int dk, int dv, gdn_dtype dtype) {
+    (void)B; (void)Hk; (void)Hv; (void)dk; (void)dv; (void)dtype;
+    return kSequentialMaxTokens;
 }
 
 gdn_status gdn_prefill_qknorm(const void* q, const void* k, const void* v, const float* g,
@@ -174,7 +207,7 @@ gdn_status gdn_prefill_qknorm(const void* q, const void* k, const void* v, const
                               int chunk, gdn_dtype dtype, void* workspace,
                               size_t workspace_bytes, void* stream) {
     return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
-                          dtype, workspace, workspace_bytes, stream, 3, 1);
+                          dtype, workspace, workspace_bytes, stream, 3, 1, false);
 }
 
 gdn_status gdn_prefill_prepare(const void* q, const void* k, const void* v, const float* g,
@@ -183,7 +216,7 @@ gdn_status gdn_prefill_prepare(const void* q, const void* k, const void* v, cons
                                int chunk, gdn_dtype dtype, void* workspace,
                                size_t workspace_bytes, void* stream) {
     return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
-                          dtype, workspace, workspace_bytes, stream, 1, 0);
+                          dtype, workspace, workspace_bytes, stream, 1, 0, false);
 }
 
 gdn_status gdn_prefill_scan(const void* q, const void* k, const void* v, const float* g,
@@ -192,7 +225,7 @@ gdn_status gdn_prefill_scan(const void* q, const void* k, const void* v, const f
                             gdn_dtype dtype, void* workspace, size_t workspace_bytes,
                             void* stream) {
     return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
-                          dtype, workspace, workspace_bytes, stream, 2, 0);
+                          dtype, workspace, workspace_bytes, stream, 2, 0, false);
 }
 
 }  // extern "C"

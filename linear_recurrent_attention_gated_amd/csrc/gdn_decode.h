@@ -37,32 +37,6 @@ struct DecodeParams {
     int qk_norm;          // nonzero: q and k are L2-normalised per head first
 };
 
-// Sum over each aligned group of L lanes (L = 8, 16 or 32), returned to every lane of the
-// group: two quad permutations, the half-row and row mirrors (DPP, on the VALU), and for 32
-// the gfx950 row swap.  Every lane adds the same two partial sums (in either order), so all
-// lanes of a group hold the bitwise-same result.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-
-template <int L>
-__device__ __forceinline__ float group_sum(float x) {
-    static_assert(L == 8 || L == 16 || L == 32, "group size");
-    x += dpp_f<0xB1>(x);    // quad_perm [1,0,3,2]: partner lane ^ 1
-    x += dpp_f<0x4E>(x);    // quad_perm [2,3,0,1]: partner lane ^ 2
-    x += dpp_f<0x141>(x);   // row_half_mirror: the other quad of each 8 lanes
-    if constexpr (L >= 16) x += dpp_f<0x140>(x);   // row_mirror: the other half of each 16
-    if constexpr (L >= 32) {
-        // swap odd rows of one copy with even rows of the other: the pair of results holds,
-        // in every lane, its own row's value and its partner row's (rows of 16 lanes)
-        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
-                                                        false, false);
-        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-    return x;
-}
-
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     using X = Elem<E>;

@@ -134,6 +134,65 @@ __device__ __forceinline__ float frag_elem(float f, int) { return f; }
 // L2 normalisation of q and k, x / sqrt(|x|^2 + eps): eps keeps a zero vector finite
 constexpr float kNormEps = 1e-6f;
 
+// Sum over each aligned group of L lanes (L = 4, 8, 16 or 32), returned to every lane of the
+// group: two quad permutations, the half-row and row mirrors (DPP, on the VALU), and for 32
+// the gfx950 row swap.  Every lane adds the same two partial sums (in either order), so all
+// lanes of a group hold the bitwise-same result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+template <int L>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(L == 4 || L == 8 || L == 16 || L == 32, "group size");
+    x += dpp_f<0xB1>(x);    // quad_perm [1,0,3,2]: partner lane ^ 1
+    x += dpp_f<0x4E>(x);    // quad_perm [2,3,0,1]: partner lane ^ 2
+    if constexpr (L >= 8) x += dpp_f<0x141>(x);   // row_half_mirror: the other quad of each 8
+    if constexpr (L >= 16) x += dpp_f<0x140>(x);   // row_mirror: the other half of each 16
+    if constexpr (L >= 32) {
+        // swap odd rows of one copy with even rows of the other: the pair of results holds,
+        // in every lane, its own row's value and its partner row's (rows of 16 lanes)
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                        false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    return x;
+}
+
+// group_sum of two and of three independent values, one reduction step of each in turn (the
+// DPP reads of one hide the wait states after the adds of the others)
+template <int L>
+__device__ __forceinline__ void group_sum2(float& x, float& y) {
+    static_assert(L == 4 || L == 8 || L == 16 || L == 32, "group size");
+    x += dpp_f<0xB1>(x); y += dpp_f<0xB1>(y);
+    x += dpp_f<0x4E>(x); y += dpp_f<0x4E>(y);
+    if constexpr (L >= 8) { x += dpp_f<0x141>(x); y += dpp_f<0x141>(y); }
+    if constexpr (L >= 16) { x += dpp_f<0x140>(x); y += dpp_f<0x140>(y); }
+    if constexpr (L >= 32) {
+        const auto rx = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        const auto ry = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+        x = __uint_as_float(rx[0]) + __uint_as_float(rx[1]);
+        y = __uint_as_float(ry[0]) + __uint_as_float(ry[1]);
+    }
+}
+template <int L>
+__device__ __forceinline__ void group_sum3(float& x, float& y, float& z) {
+    static_assert(L == 4 || L == 8 || L == 16 || L == 32, "group size");
+    x += dpp_f<0xB1>(x); y += dpp_f<0xB1>(y); z += dpp_f<0xB1>(z);
+    x += dpp_f<0x4E>(x); y += dpp_f<0x4E>(y); z += dpp_f<0x4E>(z);
+    if constexpr (L >= 8) { x += dpp_f<0x141>(x); y += dpp_f<0x141>(y); z += dpp_f<0x141>(z); }
+    if constexpr (L >= 16) { x += dpp_f<0x140>(x); y += dpp_f<0x140>(y); z += dpp_f<0x140>(z); }
+    if constexpr (L >= 32) {
+        const auto rx = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        const auto ry = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+        const auto rz = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(z), false, false);
+        x = __uint_as_float(rx[0]) + __uint_as_float(rx[1]);
+        y = __uint_as_float(ry[0]) + __uint_as_float(ry[1]);
+        z = __uint_as_float(rz[0]) + __uint_as_float(rz[1]);
+    }
+}
+
 // Workgroup barrier for LDS traffic: wait until this wave's LDS reads and writes have
 // completed, then synchronise the waves.  Unlike __syncthreads() it does not wait for
 // outstanding global loads or stores, so prefetches and output stores stay in flight across

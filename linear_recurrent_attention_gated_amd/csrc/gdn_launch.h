@@ -18,6 +18,11 @@ hipError_t prefill_f32_c16(int dk, int dv, const PrefillParams& p, int stages, h
 hipError_t prefill_f32_c32(int dk, int dv, const PrefillParams& p, int stages, hipStream_t s);
 hipError_t prefill_f32_c64(int dk, int dv, const PrefillParams& p, int stages, hipStream_t s);
 
+// Token-sequential prefill (gdn_sequential.h); uses the q, k, v, g, beta, state, o, size,
+// Ts / t0 and qk_norm fields of p, no workspace.
+hipError_t sequential_bf16(int dk, int dv, const PrefillParams& p, hipStream_t s);
+hipError_t sequential_f32(int dk, int dv, const PrefillParams& p, hipStream_t s);
+
 hipError_t decode_bf16(int dk, int dv, const DecodeParams& p, hipStream_t s);
 hipError_t decode_f32(int dk, int dv, const DecodeParams& p, hipStream_t s);
 

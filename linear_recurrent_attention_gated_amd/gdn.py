@@ -18,9 +18,15 @@ GDN_BF16 = 0
 GDN_F32 = 1
 _STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
            4: "GDN_ERR_ALIGN", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP"}
-EXPORTS = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_qknorm", "gdn_prefill_prepare",
-           "gdn_prefill_scan", "gdn_decode_step", "gdn_decode_step_qknorm", "gdn_status_string",
-           "gdn_abi_version")
+EXPORTS = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_qknorm", "gdn_prefill_ex",
+           "gdn_prefill_sequential_max_tokens", "gdn_prefill_prepare", "gdn_prefill_scan",
+           "gdn_decode_step", "gdn_decode_step_qknorm", "gdn_status_string", "gdn_abi_version")
+
+# flags of gdn_prefill_ex
+GDN_QK_NORM = 1
+GDN_PATH_SEQUENTIAL = 2
+GDN_PATH_AUTO = 4
+PATHS = {"blockwise": 0, "sequential": GDN_PATH_SEQUENTIAL, "auto": GDN_PATH_AUTO}
 
 
 class GdnError(RuntimeError):
@@ -49,6 +55,10 @@ def lib():
         for fn in ("gdn_decode_step", "gdn_decode_step_qknorm"):
             getattr(L, fn).argtypes = [P] * 8 + [I] * 6 + [P]
             getattr(L, fn).restype = I
+        L.gdn_prefill_ex.argtypes = [P] * 8 + [I] * 8 + [P, Z, P, ctypes.c_uint]
+        L.gdn_prefill_ex.restype = I
+        L.gdn_prefill_sequential_max_tokens.argtypes = [I] * 6
+        L.gdn_prefill_sequential_max_tokens.restype = I
         L.gdn_status_string.argtypes = [I]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
@@ -116,6 +126,19 @@ def gdn_prefill_qknorm(q, k, v, g, beta, state_in, o, state_out, chunk, workspac
                   workspace, stream)
 
 
+def gdn_prefill_ex(q, k, v, g, beta, state_in, o, state_out, chunk, workspace, flags, stream=None):
+    """Calls gdn_prefill_ex (flags: GDN_QK_NORM | GDN_PATH_SEQUENTIAL or GDN_PATH_AUTO);
+    arguments as gdn_prefill, the workspace may be None on the sequential path."""
+    _prefill_call("gdn_prefill_ex", q, k, v, g, beta, state_in, o, state_out, chunk, workspace,
+                  stream, (int(flags),))
+
+
+def gdn_prefill_sequential_max_tokens(B, Hk, Hv, dk, dv, dtype) -> int:
+    if isinstance(dtype, torch.dtype):
+        dtype = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
+    return int(lib().gdn_prefill_sequential_max_tokens(B, Hk, Hv, dk, dv, dtype))
+
+
 def gdn_prefill_prepare(q, k, v, g, beta, state_in, o, state_out, chunk, workspace, stream=None):
     """Calls gdn_prefill_prepare (the state-independent stage); arguments as gdn_prefill."""
     _prefill_call("gdn_prefill_prepare", q, k, v, g, beta, state_in, o, state_out, chunk,
@@ -128,7 +151,8 @@ def gdn_prefill_scan(q, k, v, g, beta, state_in, o, state_out, chunk, workspace,
                   stream)
 
 
-def _prefill_call(fn, q, k, v, g, beta, state_in, o, state_out, chunk, workspace, stream):
+def _prefill_call(fn, q, k, v, g, beta, state_in, o, state_out, chunk, workspace, stream,
+                  extra=()):
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
     dt = _dt(q)
@@ -145,7 +169,7 @@ def _prefill_call(fn, q, k, v, g, beta, state_in, o, state_out, chunk, workspace
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = getattr(lib(), fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
                             _ptr(o), _ptr(state_out), B, T, Hk, Hv, dk, dv, int(chunk), dt,
-                            _ptr(workspace), ws_bytes, _stream(stream))
+                            _ptr(workspace), ws_bytes, _stream(stream), *extra)
     if rc != 0:
         raise GdnError(fn, rc)
 
@@ -183,18 +207,26 @@ def _decode_call(fn, q, k, v, g, beta, state_in, state_out, o, stream):
 
 # -- conveniences that allocate outputs with torch --------------------------------------------
 
-def prefill(q, k, v, g, beta, state=None, chunk=64, workspace=None, stream=None, qk_norm=False):
-    """Returns (o, state_out); allocates o, state_out and (if not given) the workspace.
-    qk_norm: L2-normalise q and k inside the kernels (gdn_prefill_qknorm)."""
+def prefill(q, k, v, g, beta, state=None, chunk=64, workspace=None, stream=None, qk_norm=False,
+            path="blockwise"):
+    """Returns (o, state_out); allocates o, state_out and (if needed and not given) the
+    workspace.  qk_norm: L2-normalise q and k inside the kernels.  path: "blockwise"
+    (gdn_prefill / gdn_prefill_qknorm), "sequential" or "auto" (gdn_prefill_ex)."""
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
     o = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=q.device)
     s_out = torch.empty((B, Hv, dv, dk), dtype=torch.float32, device=q.device)
-    if workspace is None and T > 0:
+    flags = PATHS[path] | (GDN_QK_NORM if qk_norm else 0)
+    seq = path == "sequential" or (
+        path == "auto" and T <= gdn_prefill_sequential_max_tokens(B, Hk, Hv, dk, dv, q.dtype))
+    if workspace is None and T > 0 and not seq:
         nb = gdn_prefill_workspace_bytes(B, T, Hk, Hv, dk, dv, chunk, q.dtype)
         workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
-    (gdn_prefill_qknorm if qk_norm else gdn_prefill)(q, k, v, g, beta, state, o, s_out, chunk,
-                                                     workspace, stream)
+    if path == "blockwise":
+        (gdn_prefill_qknorm if qk_norm else gdn_prefill)(q, k, v, g, beta, state, o, s_out, chunk,
+                                                         workspace, stream)
+    else:
+        gdn_prefill_ex(q, k, v, g, beta, state, o, s_out, chunk, workspace, flags, stream)
     return o, s_out
 
 

@@ -99,6 +99,33 @@ def test_prefill_rejects(kw, code, fn):
     assert _prefill(fn=fn, **kw) == code
 
 
+@pytest.mark.parametrize("flags", [8, 2 | 4, 0x100])
+def test_prefill_ex_rejects_flags(flags):
+    L = gdn.lib()
+    ws = gdn.gdn_prefill_workspace_bytes(1, 64, 2, 4, 32, 32, 16, 0)
+    rc = L.gdn_prefill_ex(BASE, BASE + 10 * MB, BASE + 20 * MB, BASE + 40 * MB, BASE + 41 * MB,
+                          BASE + 50 * MB, BASE + 60 * MB, BASE + 80 * MB, 1, 64, 2, 4, 32, 32, 16,
+                          0, BASE + 100 * MB, ws, None, flags)
+    assert rc == 3
+
+
+@pytest.mark.parametrize("flags", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("kw,code", [(dict(q=None), 1), (dict(Hv=3), 2), (dict(dk=48), 3),
+                                     (dict(q=BASE + 2), 4), (dict(o=BASE + 10 * MB), 5)])
+def test_prefill_ex_validates_on_every_path(kw, code, flags):
+    a = dict(q=BASE, o=BASE + 60 * MB, Hv=4, dk=32)
+    a.update(kw)
+    rc = gdn.lib().gdn_prefill_ex(a["q"], BASE + 10 * MB, BASE + 20 * MB, BASE + 40 * MB,
+                                  BASE + 41 * MB, BASE + 50 * MB, a["o"], BASE + 80 * MB, 1, 64,
+                                  2, a["Hv"], a["dk"], 32, 16, 0, BASE + 100 * MB, 1 << 26, None,
+                                  flags)
+    assert rc == code
+
+
+def test_sequential_crossover_is_positive():
+    assert gdn.gdn_prefill_sequential_max_tokens(1, 16, 32, 128, 128, 0) >= 1
+
+
 DECODE_ERRORS = [
     (dict(state_in=None), 1), (dict(o=None), 1),
     (dict(Hv=5), 2), (dict(B=0), 2),
