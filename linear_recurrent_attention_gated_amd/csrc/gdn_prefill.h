@@ -351,7 +351,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             if (lane == 0) gf[2 * C] = exp2f(gl2);
         }
     }
-    load_kvg(nxt);   // registers consumed above; the next item's rows are in flight from here
+    if (more) load_kvg(nxt);   // registers consumed above; the next item's rows are in flight from here
 #pragma unroll
     for (int kb = 0; kb < NKD; ++kb) qf[kb] = X::keep_if(qf[kb], pm_ld * 16 + rl < n);
     lds_barrier();   // (B1)
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int q = 0; q < NT / 2; ++q) G1[q] = kk_tile(2 * q + 1, 2 * q);
         p_row(0);
-        load_q(nxt);
+        if (more) load_q(nxt);
 #pragma unroll
         for (int d = 0; d < NT; ++d) mask_a(d, d, Gd[d]);
 #pragma unroll
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
     } else {
         if (has_prow) p_row(pm);
-        load_q(nxt);
+        if (more) load_q(nxt);
         if (NT == 4 && wave >= 2) {   // the 32x32 off-diagonal block, one tile column per wave
             const int tn = wave - 2;
             const f32x4 Ga = kk_tile(2, tn), Gb = kk_tile(3, tn);
