@@ -143,14 +143,15 @@ def summarize_counters(fetch_dir, write_dir):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=6, help="rotating input buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=None)
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run one plain device-to-device copy of known size (the reference "
-                         "point for the HBM byte counters)")
+                    help="accepted for older command lines: the plain device-to-device copy of "
+                         "known size (the reference point for the HBM byte counters and the "
+                         "achievable-bandwidth figure) now runs in every measurement")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script "
                          "with --copy-calibration into profiles/hbm_traffic.txt, then exit")
@@ -161,7 +162,8 @@ def parse():
     return ap.parse_args()
 
 
-CROSSOVER_T = (1, 8, 16, 32, 64, 96, 128, 192, 256, 512, 1024, 4096, 16384, 131072)
+# short prompts around the crossover, then the 10-point doubling sweep 256 .. 128K
+CROSSOVER_T = (1, 8, 16, 32, 48, 64, 96, 128, 192) + tuple(256 << i for i in range(10))
 
 
 def crossover(args):
@@ -202,6 +204,7 @@ def crossover(args):
                 if r:
                     ts.append(e0.elapsed_time(e1) * 1e3)
             res[name + "_us"] = round(float(np.median(ts)), 2)
+            res[name + "_mtok_s"] = round(T / float(np.median(ts)), 3)
         points.append(res)
         print("[crossover]", res, file=sys.stderr, flush=True)
     faster = [p["T"] for p in points if p["sequential_us"] < p["blockwise_us"]]
@@ -364,12 +367,22 @@ def main():
     tw_intra = np.array([e[0].elapsed_time(e[1]) for e in evw]) * 1e3
     tw_inter = np.array([e[1].elapsed_time(e[2]) for e in evw]) * 1e3
 
-    if args.copy_calibration:   # one plain copy of known size for the byte counters
-        src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
+    # -- achievable HBM bandwidth in the same run: a plain device-to-device copy of known
+    # size, cold (it is also the reference point of the HBM byte counters) -----------------
+    src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    copy_ms = []
+    for r in range(4):
+        scratch.fill_(r)
+        a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
         dst.copy_(src)
+        b2.record(stream)
         torch.cuda.synchronize()
-        del src, dst
+        if r:
+            copy_ms.append(a.elapsed_time(b2))
+    copy_gbs = 2 * COPY_CALIBRATION_BYTES / (min(copy_ms) * 1e-3) / 1e9
+    del src, dst
 
     mean_pf = float(t_prefill.mean())
     value = T / (mean_pf * 1e-6)
@@ -422,6 +435,8 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": pf_bytes,
+            "achievable_copy_gbs": round(copy_gbs, 1),
+            "frac_of_copy": round(achieved / copy_gbs, 4),
         },
         "decode": {
             "us_per_token_looped": round(float(t_dec.mean()), 2),
@@ -459,6 +474,16 @@ def main():
                 break
         cpu_total = time.perf_counter() - c0
         cpu_s = cpu_total / reps
+        # one thread on a bounded sample: 2 of the 32 value heads, scaled to the workload
+        c1 = time.perf_counter()
+        orc.seq(qa, ka, va, ga, ba, pairs=[(0, 0), (0, 1)], nthreads=1, rows_per_item=8)
+        one_s = (time.perf_counter() - c1) * Hv / 2
+        cpu_model = ""
+        try:
+            with open("/proc/cpuinfo") as fh:
+                cpu_model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), "")
+        except OSError:
+            pass
         o_gpu = sets[0]["o"].float().cpu().numpy()
         s_gpu = sets[0]["state_out"].cpu().numpy()
         err = lambda x, r: float(np.max(np.abs(x - r)) / np.max(np.abs(r)))  # noqa: E731
@@ -466,7 +491,11 @@ def main():
                                "kind": "oracle",
                                "sample": f"the full prefill workload (T={T}, all {Hv} value heads), "
                                          f"fp64 token-by-token scan, {threads} threads, run "
-                                         f"{reps} times in {cpu_total:.1f} s ({cpu_s:.3f} s each)"}
+                                         f"{reps} times in {cpu_total:.1f} s ({cpu_s:.3f} s each)",
+                               "single_thread_value": round(T / one_s, 1),
+                               "single_thread_sample": f"value heads 0 and 1 of the same workload on "
+                                                       f"1 thread, scaled by {Hv // 2}",
+                               "cpu_model": cpu_model, "host_cpus": ncpu}
         out["parity_vs_oracle"] = {"o": err(o_gpu, o_ref), "state": err(s_gpu, s_ref),
                                    "tol_o": 2e-2, "tol_state": 1e-2}
     print(json.dumps(out), flush=True)
