@@ -741,6 +741,8 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
     }
 
     if (chain) {
+        // the chain is the critical path: its waves win instruction arbitration on their SIMDs
+        __builtin_amdgcn_s_setprio(3);
         const E* Wg = reinterpret_cast<const E*>(p.W) + (size_t)bh * N * Sh::W_PER_CHUNK;
         const E* Ug = reinterpret_cast<const E*>(p.Ut) + (size_t)bh * N * Sh::UT_PER_CHUNK;
         const E* KTg = reinterpret_cast<const E*>(p.KT) + ((size_t)b * Hk + hk) * N * Sh::KT_PER_CHUNK;
