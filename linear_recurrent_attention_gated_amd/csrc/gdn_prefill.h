@@ -16,12 +16,12 @@
 //
 // Only exponentials of gamma_r - gamma_s with s <= r appear, so no factor can overflow.
 //
-// Kernel 1 (intra_chunk_kernel), one workgroup per (batch, value head, chunk), fully
-// parallel: Gram blocks K K^T and K Q^T on MFMA, masks with the head's gates, (I + A)
-// inverted in fp32 (16x16 diagonal blocks by substitution, then block doubling on the fp32
-// matrix cores), W and Ut on MFMA.  Everything the scan needs goes to the workspace already
-// arranged as MFMA operands (see "Workspace layout"), written straight from the
-// accumulators.
+// Kernel 1 (intra_chunk_kernel), fully parallel over (batch, value head, chunk) items, run by
+// a persistent grid that loads the next item while computing the current one: Gram blocks
+// K K^T and K Q^T on MFMA, masks with the head's gates, (I + A) inverted in fp32 (16x16
+// diagonal blocks by substitution, then block doubling on the fp32 matrix cores), W and Ut
+// on MFMA.  Everything the scan needs goes to the workspace already arranged as MFMA operands
+// (see "Workspace layout"), written straight from the accumulators.
 //
 // Kernel 2 (inter_chunk_kernel), one workgroup per (batch, value head, 16 state rows):
 // rows of S evolve independently (each needs only its own entries of v), so a head's

@@ -52,6 +52,10 @@ CASES = [
     (1, 257, 1, 2, 128, 128, 64, True),
     (1, 96, 3, 6, 64, 128, 16, True),
     (1, 200, 1, 1, 128, 32, 64, False),
+    # four and eight value heads per key head, several batches
+    (1, 150, 1, 4, 64, 64, 64, True),
+    (2, 77, 2, 8, 128, 64, 32, True),
+    (8, 40, 1, 4, 32, 32, 16, True),
 ]
 
 
@@ -116,10 +120,10 @@ def test_strong_decay_and_reset_gates():
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-@pytest.mark.parametrize("dims", [(128, 128), (64, 32), (32, 128)])
+@pytest.mark.parametrize("dims", [(128, 128), (64, 32), (32, 128), (64, 64, 1, 8)])
 def test_decode_matches_oracle(dims, dt):
-    dk, dv = dims
-    B, Hk, Hv = 3, 2, 4
+    dk, dv = dims[:2]
+    B, Hk, Hv = (3, 2, 4) if len(dims) == 2 else (2,) + tuple(dims[2:])
     d = make_inputs(B, 1, Hk, Hv, dk, dv, seed=7 + dk, dtype=DT[dt], state_std=0.1)
     say("decode", dt, dims)
     dd = to_dev(d)

@@ -26,6 +26,7 @@ CASES = [
     (2, 129, 1, 2, 64, 128, True),
     (1, 300, 2, 4, 32, 128, True),
     (1, 520, 1, 2, 128, 128, True),
+    (3, 33, 1, 4, 64, 64, True),
 ]
 
 
