@@ -449,15 +449,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             }
             return acc;
         };
+        // fragments wholly above the diagonal (tokens past row tile m) are never written: the
+        // scan does not read them
         if constexpr (KPL == 8) {
 #pragma unroll
             for (int kb = 0; kb < NKC; ++kb) {
+                if (2 * kb > m) break;
                 const frag f = X::pack(ptile(2 * kb), 2 * kb + 1 < NT ? ptile(2 * kb + 1) : zero4());
                 *reinterpret_cast<frag*>(Pg + ((size_t)(m * NKC + kb) * 64 + lane) * KPL) = f;
             }
         } else {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
+                if (t > m) break;
                 const f32x4 d = ptile(t);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) Pg[(size_t)(m * NKC + 4 * t + j) * 64 + lane] = X::from_f(d[j]);
@@ -869,6 +873,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
         }
     } else {
         const E* Pg = reinterpret_cast<const E*>(p.P) + (size_t)bh * N * Sh::P_PER_CHUNK;
+        const int pkmax = (m * 16 + 15) / KB;   // last k-block of P row tile m with nonzeros
         const E* qg = reinterpret_cast<const E*>(p.q) + (size_t)hk * DK;
         E* og = reinterpret_cast<E*>(p.o) + (size_t)h * DV + i0;
 
@@ -881,7 +886,8 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
             for (int kb = 0; kb < NKD; ++kb) op.q[kb] = X::ld(qsrc + kb * KB);   // rows past T: zeroed in the tail
             const E* psrc = Pg + (size_t)c * Sh::P_PER_CHUNK + (size_t)m * NKC * Sh::FRAG + lane * KPL;
 #pragma unroll
-            for (int kb = 0; kb < NKC; ++kb) op.p[kb] = X::ld(psrc + kb * Sh::FRAG);
+            for (int kb = 0; kb < NKC; ++kb)   // k-blocks past the diagonal are zero, not stored
+                op.p[kb] = kb <= pkmax ? X::ld(psrc + kb * Sh::FRAG) : X::zero();
         };
         auto step = [&](const OOps& op, int c, auto tailtag) {
             constexpr bool TAIL = decltype(tailtag)::value;
@@ -898,7 +904,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
                 f32x4 acc = accq * op.gr;
 #pragma unroll
                 for (int kb = 0; kb < NKC; ++kb)   // P fragments: tokens in the permuted order
-                    acc = X::mma(op.p[kb], X::ld_perm(UT + rl * LDU + X::poff(kb, g)), acc);
+                    if (kb <= pkmax) acc = X::mma(op.p[kb], X::ld_perm(UT + rl * LDU + X::poff(kb, g)), acc);
                 // O tile through LDS, written as 16-byte pieces (a token's 16 state rows are
                 // sizeof(E) pieces)
                 E* os = Os[w4];
