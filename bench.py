@@ -367,6 +367,40 @@ def main():
     tw_intra = np.array([e[0].elapsed_time(e[1]) for e in evw]) * 1e3
     tw_inter = np.array([e[1].elapsed_time(e[2]) for e in evw]) * 1e3
 
+    # -- secondary variants of the same prefill, cold: fused q/k normalisation on raw q, k
+    # (gdn_prefill_qknorm) and the all-fp32 build -------------------------------------------
+    def cold_prefill_us(fn, args_, reps):
+        ts = []
+        for i in range(reps + 1):
+            scratch.fill_(i & 0xFF)
+            a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            check(fn(*args_), "gdn_prefill variant")
+            b2.record(stream)
+            torch.cuda.synchronize()
+            if i:
+                ts.append(a.elapsed_time(b2) * 1e3)
+        return float(np.mean(ts))
+
+    from linear_recurrent_attention_gated_amd.inputs import make_inputs
+    raw = make_inputs(B, T, Hk, Hv, dk, dv, w.seed, torch.bfloat16, unit_qk=False)
+    rq, rk = raw["q"].to(dev), raw["k"].to(dev)
+    o_v = torch.empty((B, T, Hv, dv), dtype=torch.bfloat16, device=dev)   # own outputs: set 0's
+    s_v = torch.empty((B, Hv, dv, dk), dtype=torch.float32, device=dev)   # feed the parity check
+    a_qk = list(PF[0])
+    a_qk[0], a_qk[1], a_qk[6], a_qk[7] = rq.data_ptr(), rk.data_ptr(), o_v.data_ptr(), s_v.data_ptr()
+    qknorm_us = cold_prefill_us(lib.gdn_prefill_qknorm, tuple(a_qk), 10)
+    del rq, rk, raw
+    f32 = {k: host[k].float().to(dev) for k in ("q", "k", "v")}
+    o32 = torch.empty((B, T, Hv, dv), dtype=torch.float32, device=dev)
+    ws32 = torch.empty(gdn.gdn_prefill_workspace_bytes(B, T, Hk, Hv, dk, dv, C, torch.float32),
+                       dtype=torch.uint8, device=dev)
+    a32 = (f32["q"].data_ptr(), f32["k"].data_ptr(), f32["v"].data_ptr(), sets[0]["g"].data_ptr(),
+           sets[0]["beta"].data_ptr(), None, o32.data_ptr(), s_v.data_ptr(),
+           B, T, Hk, Hv, dk, dv, C, gdn.GDN_F32, ws32.data_ptr(), ws32.numel(), sh)
+    f32_us = cold_prefill_us(lib.gdn_prefill, a32, 10)
+    del f32, o32, ws32, o_v, s_v
+
     # -- achievable HBM bandwidth in the same run: a plain device-to-device copy of known
     # size, cold (it is also the reference point of the HBM byte counters) -----------------
     src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
@@ -426,6 +460,8 @@ def main():
             "inter_chunk_us": round(float(t_inter.mean()), 2),
             "warm_intra_chunk_us": round(float(tw_intra.mean()), 2),
             "warm_inter_chunk_us": round(float(tw_inter.mean()), 2),
+            "qknorm_us": round(qknorm_us, 2),
+            "f32_us": round(f32_us, 2),
             "mfma_tflops": round(pf_flops / (mean_pf * 1e-6) / 1e12, 2),
             "mfma_frac": round(pf_flops / (mean_pf * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         },
