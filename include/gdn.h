@@ -37,8 +37,9 @@
  *     before anything is enqueued.  Asynchronous kernel faults surface on the stream.
  *   - Shapes supported: dk, dv in {32, 64, 128}; Hk >= 1; Hv a multiple of Hk; B >= 1;
  *     chunk in {16, 32, 64}; any T >= 0 (a final chunk shorter than `chunk` is exact).
- *   - Thread safety: no global mutable state; concurrent calls on different streams
- *     with disjoint buffers are safe.
+ *   - Thread safety: the only global state is a per-device cache of an occupancy query,
+ *     filled idempotently on first use; concurrent calls on different streams with
+ *     disjoint buffers are safe.
  *   - Return value: a gdn_status; GDN_OK (0) on success.
  */
 #ifndef GDN_H_
