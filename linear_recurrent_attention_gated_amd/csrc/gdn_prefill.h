@@ -656,7 +656,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // state tiles.  Output waves 4..7 compute O = Gamma (Q S^T) + P U for their token tile one
 // barrier behind, from a double-buffered copy of the state, so the output products stay off
 // the chain, and write O as 16-byte pieces staged through LDS.  Each role prefetches its own
-// operands NB chunks ahead into registers.
+// operands NB chunks ahead into registers; the chain waves issue those loads just before the
+// barriers they would wait at anyway, not between a barrier and the next chunk's products.
 // SPLIT: feed the state to W S^T as a bf16 hi + lo pair (two MFMAs) so the delta U sees
 // the fp32 state to ~16 bits instead of 8.
 // ------------------------------------------------------------------------------------
@@ -751,9 +752,11 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
         const E* Ug = reinterpret_cast<const E*>(p.Ut) + (size_t)bh * N * Sh::UT_PER_CHUNK;
         const E* KTg = reinterpret_cast<const E*>(p.KT) + ((size_t)b * Hk + hk) * N * Sh::KT_PER_CHUNK;
 
-        auto fetch = [&](COps& op, int c) {
+        // the next chunk's operands are fetched in two parts, each issued where this wave
+        // would otherwise wait at a barrier: W, Ut and the update scales once U is formed,
+        // K^T and the decay once the update has read them
+        auto fetch_w = [&](COps& op, int c) {
             const float* gc = gates + (size_t)c * Sh::GATES;
-            op.gn = gc[2 * C];
             op.e = *reinterpret_cast<const f32x4*>(gc + C + m * 16 + rq);
             const E* wsrc = Wg + (size_t)c * Sh::W_PER_CHUNK + (size_t)m * NKD * Sh::FRAG + lane * KPL;
 #pragma unroll
@@ -761,6 +764,10 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
             const E* usrc = Ug + (size_t)c * Sh::UT_PER_CHUNK + (((size_t)slice * NT + m) * 64 + lane) * 4;
             if (sizeof(E) == 2) *reinterpret_cast<uint2*>(op.ut) = *reinterpret_cast<const uint2*>(usrc);
             else *reinterpret_cast<uint4*>(op.ut) = *reinterpret_cast<const uint4*>(usrc);
+        };
+        auto fetch_k = [&](COps& op, int c) {
+            const float* gc = gates + (size_t)c * Sh::GATES;
+            op.gn = gc[2 * C];
 #pragma unroll
             for (int tw = 0; tw < TPW; ++tw) {
                 const int dt = min(w4 + 4 * tw, DT - 1);
@@ -769,6 +776,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
                 for (int kb = 0; kb < NKC; ++kb) op.kt[tw][kb] = X::ld(ksrc + kb * Sh::FRAG);
             }
         };
+        auto fetch = [&](COps& op, int c) { fetch_w(op, c); fetch_k(op, c); };
 
         // state slice: S^T tiles (rows = dk index, cols = the 16 state rows of this slice)
         f32x4 St[TPW];
@@ -798,7 +806,8 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
                 }
             }
         };
-        auto step = [&](const COps& op, int c) {
+        auto step = [&](COps& op, int c, int nc, auto pftag) {
+            constexpr bool PF = decltype(pftag)::value;
             // keeps the next step's operand uses (and so their waits) out of this one
             __builtin_amdgcn_sched_barrier(0);
             const int cur = c & 1;
@@ -829,6 +838,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
                 store4(UT + rl * LDU + m * 16 + rq, u);
                 store4(UsT + rl * LDU + m * 16 + rq, us);
             }
+            if (PF) fetch_w(op, nc);
             lds_barrier();   // (B1) U complete; chunk c's slice was read from buffer cur
 #pragma unroll
             for (int tw = 0; tw < TPW; ++tw) {
@@ -841,6 +851,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
                     St[tw] = acc;
                 }
             }
+            if (PF) fetch_k(op, nc);
             publish(cur ^ 1);
             lds_barrier();   // (B2) next slice published; output waves are done with U
         };
@@ -853,14 +864,11 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
         int c = 0;
         for (; c + NBC <= N; c += NBC) {
 #pragma unroll
-            for (int j = 0; j < NBC; ++j) {
-                step(op[j], c + j);
-                fetch(op[j], min(c + j + NBC, N - 1));
-            }
+            for (int j = 0; j < NBC; ++j) step(op[j], c + j, min(c + j + NBC, N - 1), std::true_type{});
         }
 #pragma unroll
         for (int j = 0; j < NBC; ++j)
-            if (c + j < N) step(op[j], c + j);
+            if (c + j < N) step(op[j], c + j, 0, std::false_type{});
 
 #pragma unroll
         for (int tw = 0; tw < TPW; ++tw) {
