@@ -16,7 +16,8 @@
 //
 // Mapping: a row of dk floats is read by dk/4 consecutive lanes as 16-byte vectors, so
 // a wavefront reads 1 KiB of contiguous state per instruction; each thread keeps NIT
-// rows in flight before it reduces.  No matrix cores: the arithmetic is 3 FMAs per state
+// rows in flight before it reduces.  The state is read and written with the nontemporal
+// hint (it is touched once per step).  No matrix cores: the arithmetic is 3 FMAs per state
 // element against 8 bytes of traffic.
 #pragma once
 
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     float4 s[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it)
-        s[it] = *reinterpret_cast<const float4*>(p.state_in + (row0 + (size_t)it * RIT) * DK + c0);
+        s[it] = ld_stream4(p.state_in + (row0 + (size_t)it * RIT) * DK + c0);
     const E* vp = reinterpret_cast<const E*>(p.v);
     E vr[NIT];
 #pragma unroll
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         ns.y = a * s[it].y + delta * kk[1];
         ns.z = a * s[it].z + delta * kk[2];
         ns.w = a * s[it].w + delta * kk[3];
-        *reinterpret_cast<float4*>(p.state_out + row * DK + c0) = ns;
+        st_stream4(p.state_out + row * DK + c0, ns);
         if (sub == 0) op[row] = X::from_f(a * sq + delta * kq);
     }
 }

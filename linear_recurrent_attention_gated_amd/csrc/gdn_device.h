@@ -127,6 +127,18 @@ template <> struct Elem<float> {
 
 __device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
 
+// Streaming (nontemporal) 16-byte global accesses, for data a launch touches once: they carry
+// the nontemporal cache hint, under which HBM reads and writes stream faster than with the
+// default policy (a plain device copy on MI355X: ~6.2 TB/s with the hint, ~4.9 without).
+__device__ __forceinline__ float4 ld_stream4(const float* p) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void st_stream4(float* p, float4 v) {
+    const f32x4 x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
+}
+
 // element e of an operand fragment, as stored
 __device__ __forceinline__ bf16_t frag_elem(bf16x8 f, int e) { return __builtin_bit_cast(u16x8, f)[e]; }
 __device__ __forceinline__ float frag_elem(float f, int) { return f; }
