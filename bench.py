@@ -99,9 +99,14 @@ def summarize_counters(fetch_dir, write_dir):
                     if row.get("Counter_Name") != counter:
                         continue
                     name = row.get("Kernel_Name", "")
+                    # the bench also runs the fused-normalisation and all-fp32 prefills: their
+                    # kernels are other template instances, kept apart by name
+                    el = "f32" if "<float" in name else "bf16"
                     key = ("copy" if "copybuffer" in name.lower()
-                           else "inter" if "inter_chunk_kernel" in name
-                           else "intra" if "intra_chunk_kernel" in name
+                           else ("inter" if el == "bf16" else "inter_f32")
+                           if "inter_chunk_kernel" in name
+                           else ("intra_qknorm" if ", true>" in name else "intra") + ("" if el == "bf16" else "_f32")
+                           if "intra_chunk_kernel" in name
                            else "decode_L%d" % (int(float(row.get("Grid_Size", "0"))) // (256 * 256))
                            if "decode_kernel" in name else None)
                     if key is None:
@@ -122,7 +127,9 @@ def summarize_counters(fetch_dir, write_dir):
              "#   python bench.py --summarize-counters %s %s" % (fetch_dir, write_dir),
              "# Raw counter bytes are divided by the factor the same counter reads for a plain",
              "# device-to-device copy of %d bytes (read and written once)." % COPY_CALIBRATION_BYTES,
-             "# decode_L<n>: one decode launch over n layers (B = n).",
+             "# intra, inter: the bf16 prefill (the inter kernel also serves the fused-normalisation",
+             "# prefill, intra_qknorm); *_f32: the all-fp32 prefill; prefill_bytes_per_launch = intra",
+             "# + inter.  decode_L<n>: one decode launch over n layers (B = n).",
              "source_hash: %s" % kernel_source_hash(),
              "fetch_scale: %.4f" % f_scale, "write_scale: %.4f" % w_scale]
     for k in sorted(set(fetch) | set(write)):
