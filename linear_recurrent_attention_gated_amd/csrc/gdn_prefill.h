@@ -40,6 +40,8 @@
 //   W   [B][Hv][N][C/16][DK/KB] fragments   A operand of W S^T   (rows tokens, k = dk; permuted)
 //   P   [B][Hv][N][C/16][NKC]   fragments   A operand of P U     (rows tokens, k = tokens; permuted)
 //   KT  [B][Hk][N][DK/16][NKC]  fragments   A operand of K^T U'  (rows dk,     k = tokens; permuted)
+//   QF  [B][Hk][N][C/16][DK/KB] fragments   A operand of Q S^T   (rows tokens, k = dk) -- the raw q
+//       rows in the layout W uses, so the scan reads them contiguously
 //   Ut  [B][Hv][N][DV/16][C/16] accumulator tiles (lane: col l % 16, rows 4 (l/16) + [0,4))
 //   gam [B][Hv][N][2C + 4] fp32 gate factors per chunk: [0, C) the output scale exp(gamma_r),
 //       [C, 2C) the update scale exp(gamma_last - gamma_r), [2C] the chunk decay
@@ -69,6 +71,7 @@ struct PrefillParams {
     void* Ut;
     void* P;
     void* KT;
+    void* QF;     // Q row tiles as MFMA fragments, per key head (see the workspace layout)
     float* gam;   // gate factors (see the workspace layout)
     int B, T, Hk, Hv, N;  // T = tokens of this pass, N = its number of chunks
     // Token t of batch b of this pass is token Ts * b + t0 + t of q, k, v, g, beta and o
@@ -469,6 +472,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
     };
 
+    // this wave's Q row tile m as fragments for the scan's output products, once per key head
+    // (rows past the chunk are zero)
+    auto store_qf = [&](int m) {
+        if (h % grp != 0) return;
+        E* QFg = reinterpret_cast<E*>(p.QF) + (((size_t)b * Hk + hk) * N + c) * S::W_PER_CHUNK;
+#pragma unroll
+        for (int kb = 0; kb < NKD; ++kb)
+            *reinterpret_cast<frag*>(QFg + ((size_t)(m * NKD + kb) * 64 + lane) * KPL) = qf[kb];
+    };
+
     // ---- phase 2 -------------------------------------------------------------------------------
     if (wave == 0) {
         f32x4 Gd[NT], G1[NT / 2 > 0 ? NT / 2 : 1];
@@ -477,6 +490,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int q = 0; q < NT / 2; ++q) G1[q] = kk_tile(2 * q + 1, 2 * q);
         p_row(0);
+        store_qf(0);
         if (more) load_q(nxt);
 #pragma unroll
         for (int d = 0; d < NT; ++d) mask_a(d, d, Gd[d]);
@@ -525,7 +539,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             for (int j = 0; j < 4; ++j) sR[(hi + rq + j) * LDR + lo + rl] = -r21[j];
         }
     } else {
-        if (has_prow) p_row(pm);
+        if (has_prow) {
+            p_row(pm);
+            store_qf(pm);
+        }
         if (more) load_q(nxt);
         if (NT == 4 && wave >= 2) {   // the 32x32 off-diagonal block, one tile column per wave
             const int tn = wave - 2;
@@ -882,16 +899,16 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
     } else {
         const E* Pg = reinterpret_cast<const E*>(p.P) + (size_t)bh * N * Sh::P_PER_CHUNK;
         const int pkmax = (m * 16 + 15) / KB;   // last k-block of P row tile m with nonzeros
-        const E* qg = reinterpret_cast<const E*>(p.q) + (size_t)hk * DK;
+        const E* qfg = reinterpret_cast<const E*>(p.QF) + ((size_t)b * Hk + hk) * N * Sh::W_PER_CHUNK
+                       + ((size_t)m * NKD * 64 + lane) * KPL;
         E* og = reinterpret_cast<E*>(p.o) + (size_t)h * DV + i0;
 
         auto fetch = [&](OOps& op, int c) {
             const int t0 = c * C;
             op.gr = *reinterpret_cast<const f32x4*>(gates + (size_t)c * Sh::GATES + m * 16 + rq);
-            const int tq = t0 + m * 16 + rl;
-            const E* qsrc = qg + ((size_t)b * p.Ts + p.t0 + min(tq, T - 1)) * Hk * DK + kq;
+            const E* qsrc = qfg + (size_t)c * Sh::W_PER_CHUNK;
 #pragma unroll
-            for (int kb = 0; kb < NKD; ++kb) op.q[kb] = X::ld(qsrc + kb * KB);   // rows past T: zeroed in the tail
+            for (int kb = 0; kb < NKD; ++kb) op.q[kb] = X::ld(qsrc + (size_t)kb * Sh::FRAG);
             const E* psrc = Pg + (size_t)c * Sh::P_PER_CHUNK + (size_t)m * NKC * Sh::FRAG + lane * KPL;
 #pragma unroll
             for (int kb = 0; kb < NKC; ++kb)   // k-blocks past the diagonal are zero, not stored
