@@ -259,9 +259,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             const int idx = min(tid * PV + i, C * VV - 1), r = idx % C, cv = idx / C;
             vr[i] = *reinterpret_cast<const uint4*>(vg + (size_t)min(r, n - 1) * rsv + cv * EPV);
         }
-        const size_t gidx = ((size_t)it.b * p.Ts + p.t0 + t0 + min(lane, n - 1)) * Hv + it.h;
-        graw = p.g[gidx];
-        braw = p.beta[gidx];
+        // the gates go to wave 0 alone, which scans them (a token's gates of all heads share a
+        // 128-byte line, so each of these loads touches 64 lines)
+        if (wave == 0) {
+            const size_t gidx = ((size_t)it.b * p.Ts + p.t0 + t0 + min(lane, n - 1)) * Hv + it.h;
+            graw = p.g[gidx];
+            braw = p.beta[gidx];
+        }
     };
     auto load_q = [&](const Item& it) {
         const int t0 = it.c * C, n = min(C, T - t0);
