@@ -70,7 +70,7 @@ typedef enum {
  * T == 0).  Returns 0 also for unsupported arguments (gdn_prefill then reports the reason).
  * The workspace holds the per-chunk blocks of the blockwise form between its two kernels;
  * its content on entry is irrelevant and on exit unspecified.  It grows linearly with B * T
- * (about 113 MiB at B = 1, T = 4096, Hk = 16, Hv = 32, dk = dv = 128, bf16). */
+ * (about 81 MiB at B = 1, T = 4096, Hk = 16, Hv = 32, dk = dv = 128, bf16). */
 size_t gdn_prefill_workspace_bytes(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                                    gdn_dtype dtype);
 
@@ -147,12 +147,14 @@ int gdn_prefill_sequential_max_tokens(int B, int Hk, int Hv, int dk, int dv, gdn
  * stage).  Same arguments and rules as gdn_prefill, except that they need the one-pass
  * workspace (gdn_prefill_workspace_bytes); gdn_prefill == prepare then scan on one stream
  * with one workspace.
- *   gdn_prefill_prepare: the state-independent per-chunk blocks (decay-masked Gram, the
- *     unit-triangular inverse, the W / U~ blocks, the masked query-key block, q rearranged
- *     for the scan), written to the workspace.  Reads q, k, v, g, beta; ignores state_in, o
- *     and state_out (they still take part in the overlap checks).
+ *   gdn_prefill_prepare: the state-independent per-chunk blocks (decay-masked Gram and its
+ *     unit-triangular inverse, folded with the gates and beta into the blocks that update
+ *     the state and form the output from the chunk's residual v - decayed prediction; k
+ *     and q rearranged for the scan), written to the workspace.  Reads q, k, g, beta, and
+ *     v only to bring it into the cache for the scan; ignores state_in, o and state_out
+ *     (they still take part in the overlap checks).
  *   gdn_prefill_scan: carries the state across the chunks in order and writes o and
- *     state_out.  Reads state_in and what gdn_prefill_prepare left in the workspace
+ *     state_out.  Reads state_in, v and what gdn_prefill_prepare left in the workspace
  *     for the same q, k, v, g, beta and sizes; the workspace must not be modified in
  *     between.  T == 0: state copy, as gdn_prefill. */
 gdn_status gdn_prefill_prepare(const void *q, const void *k, const void *v, const float *g,

@@ -31,9 +31,9 @@ constexpr int kSequentialMaxTokens = 56;
 
 // Workspace regions of the blockwise prefill (see gdn_prefill.h).
 struct Layout {
-    size_t W, Ut, P, KT, QF, gam, total;
+    size_t KF, QF, Z, P, gam, total;
 };
-Layout layout(int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype dt) {
+Layout layout(int B, int T, int Hk, int Hv, int dk, int /*dv*/, int chunk, gdn_dtype dt) {
     const size_t es = elem_size(dt);
     const size_t N = ((size_t)T + chunk - 1) / chunk, Tp = N * (size_t)chunk;
     // token-side k-blocks of the MFMA fragments are padded to 32 (bf16) / 4 (fp32) tokens
@@ -41,11 +41,10 @@ Layout layout(int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype
     const size_t cp = ((size_t)chunk + kb - 1) / kb * kb;
     Layout L;
     size_t off = 0;
-    L.W = off;   off = round_up(off + (size_t)B * Hv * Tp * dk * es, 256);
-    L.Ut = off;  off = round_up(off + (size_t)B * Hv * Tp * dv * es, 256);
-    L.P = off;   off = round_up(off + (size_t)B * Hv * Tp * cp * es, 256);
-    L.KT = off;  off = round_up(off + (size_t)B * Hk * N * dk * cp * es, 256);
+    L.KF = off;  off = round_up(off + (size_t)B * Hk * Tp * dk * es, 256);
     L.QF = off;  off = round_up(off + (size_t)B * Hk * Tp * dk * es, 256);
+    L.Z = off;   off = round_up(off + (size_t)B * Hv * N * dk * cp * es, 256);
+    L.P = off;   off = round_up(off + (size_t)B * Hv * Tp * cp * es, 256);
     L.gam = off; off = round_up(off + (size_t)B * Hv * N * (2 * chunk + 4) * sizeof(float), 256);
     L.total = off;
     return L;
@@ -149,7 +148,7 @@ gdn_status prefill_stages(const void* q, const void* k, const void* v, const flo
         p.state_in = t0 == 0 ? state_in : state_out;
         p.o = o; p.state_out = state_out;
         char* ws = static_cast<char*>(workspace);
-        p.W = ws + L.W; p.Ut = ws + L.Ut; p.P = ws + L.P; p.KT = ws + L.KT; p.QF = ws + L.QF;
+        p.KF = ws + L.KF; p.QF = ws + L.QF; p.Z = ws + L.Z; p.P = ws + L.P;
         p.gam = reinterpret_cast<float*>(ws + L.gam);
         p.B = B; p.T = Tp; p.Hk = Hk; p.Hv = Hv; p.N = (Tp + chunk - 1) / chunk;
         p.Ts = T; p.t0 = t0;

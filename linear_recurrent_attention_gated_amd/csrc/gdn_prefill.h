@@ -8,19 +8,26 @@
 //
 //   A[r,s] = beta_r exp(gamma_r - gamma_s) (k_r . k_s),  s < r      (decay-masked Gram)
 //   R      = (I + A)^-1                                           (unit lower triangular)
-//   W      = R diag(beta Gamma) K,      Ut = R diag(beta) V         (state independent)
 //   P[r,s] = exp(gamma_r - gamma_s) (q_r . k_s),  s <= r
-//   U      = Ut - W S0^T                                          (deltas of the chunk)
+//   U      = R diag(beta) (V - diag(Gamma) K S0^T)                  (deltas of the chunk)
 //   O      = diag(Gamma) Q S0^T + P U
 //   S_next = Gamma_{n-1} S0 + U^T diag(exp(gamma_{n-1} - gamma)) K
 //
 // Only exponentials of gamma_r - gamma_s with s <= r appear, so no factor can overflow.
+// The state-independent factors are gathered around the residual Y = V - diag(Gamma) K S0^T
+// (the values minus what the decayed state predicts for the chunk's keys):
+//
+//   Z   = K^T diag(exp(gamma_{n-1} - gamma)) R diag(beta)             (dk x n)
+//   P'  = P R diag(beta)                                            (n x n, lower triangular)
+//   S_next^T = Gamma_{n-1} S0^T + Z Y,      O = diag(Gamma) Q S0^T + P' Y
+//
+// so the scan reads v itself and nothing derived from it.
 //
 // Kernel 1 (intra_chunk_kernel), fully parallel over (batch, value head, chunk) items, run by
 // a persistent grid that loads the next item while computing the current one: Gram blocks
 // K K^T and K Q^T on MFMA, masks with the head's gates, (I + A) inverted in fp32 (16x16
-// diagonal blocks by substitution, then block doubling on the fp32 matrix cores), W and Ut
-// on MFMA.  Everything the scan needs goes to the workspace already arranged as MFMA operands
+// diagonal blocks by substitution, then block doubling on the fp32 matrix cores), Z and P' on
+// MFMA.  Everything the scan needs goes to the workspace already arranged as MFMA operands
 // (see "Workspace layout"), written straight from the accumulators.
 //
 // Kernel 2 (inter_chunk_kernel), one workgroup per (batch, value head, 16 state rows):
@@ -37,16 +44,16 @@
 // k = kb * KB + g * KPL + [0, KPL).  The permuted order is the one an accumulator tile
 // provides without lane exchanges (see gdn_device.h), and the scan reads the matching
 // operand in the same order.
-//   W   [B][Hv][N][C/16][DK/KB] fragments   A operand of W S^T   (rows tokens, k = dk; permuted)
-//   P   [B][Hv][N][C/16][NKC]   fragments   A operand of P U     (rows tokens, k = tokens; permuted)
-//   KT  [B][Hk][N][DK/16][NKC]  fragments   A operand of K^T U'  (rows dk,     k = tokens; permuted)
+//   KF  [B][Hk][N][C/16][DK/KB] fragments   A operand of K S^T   (rows tokens, k = dk) -- the raw k
+//       rows (zero past the chunk's end), so the scan reads them contiguously
 //   QF  [B][Hk][N][C/16][DK/KB] fragments   A operand of Q S^T   (rows tokens, k = dk) -- the raw q
-//       rows in the layout W uses, so the scan reads them contiguously
-//   Ut  [B][Hv][N][DV/16][C/16] accumulator tiles (lane: col l % 16, rows 4 (l/16) + [0,4))
+//       rows, likewise
+//   Z   [B][Hv][N][DK/16][NKC]  fragments   A operand of Z Y     (rows dk,     k = tokens; permuted)
+//   P   [B][Hv][N][C/16][NKC]   fragments   A operand of P' Y    (rows tokens, k = tokens; permuted)
 //   gam [B][Hv][N][2C + 4] fp32 gate factors per chunk: [0, C) the output scale exp(gamma_r),
-//       [C, 2C) the update scale exp(gamma_last - gamma_r), [2C] the chunk decay
-//       exp(gamma_last) (rows past the end repeat the last row's gamma).  With fused q/k
-//       normalisation the output scale also carries 1 / |q_r| and the update scale 1 / |k_r|.
+//       [C, 2C) the key-row scale exp(gamma_r) of Y, [2C] the chunk decay exp(gamma_last)
+//       (rows past the end repeat the last row's gamma).  With fused q/k normalisation the
+//       output scale also carries 1 / |q_r| and the key-row scale 1 / |k_r|.
 // NKC = ceil(C / KB); k-values past the chunk are stored as zeros.
 #pragma once
 
@@ -67,11 +74,10 @@ struct PrefillParams {
     const float* state_in;
     void* o;
     float* state_out;
-    void* W;
-    void* Ut;
-    void* P;
-    void* KT;
-    void* QF;     // Q row tiles as MFMA fragments, per key head (see the workspace layout)
+    void* KF;     // K row tiles as MFMA fragments, per key head (see the workspace layout)
+    void* QF;     // Q row tiles as MFMA fragments, per key head
+    void* Z;      // K^T diag(e) R diag(beta) as fragments, per value head
+    void* P;      // P R diag(beta) as fragments, per value head
     float* gam;   // gate factors (see the workspace layout)
     int B, T, Hk, Hv, N;  // T = tokens of this pass, N = its number of chunks
     // Token t of batch b of this pass is token Ts * b + t0 + t of q, k, v, g, beta and o
@@ -94,8 +100,7 @@ struct PrefillShape {
     static constexpr int FRAG = 64 * KPL;                   // elements per fragment
     static constexpr size_t W_PER_CHUNK = (size_t)NT * NKD * FRAG;
     static constexpr size_t P_PER_CHUNK = (size_t)NT * NKC * FRAG;
-    static constexpr size_t KT_PER_CHUNK = (size_t)(DK / 16) * NKC * FRAG;
-    static constexpr size_t UT_PER_CHUNK = (size_t)(DV / 16) * NT * 256;
+    static constexpr size_t Z_PER_CHUNK = (size_t)(DK / 16) * NKC * FRAG;
     static constexpr int GATES = 2 * C + 4;   // fp32 gate factors per chunk (16-byte multiple)
 };
 
@@ -143,24 +148,25 @@ __device__ __forceinline__ void store_run(E* dst, const E (&v)[8], int np) {
 }
 
 // ------------------------------------------------------------------------------------
-// Kernel 1: per-chunk, state-independent blocks; one workgroup per (batch, value head,
+// Kernel 1: per-chunk, state-independent blocks; one work item per (batch, value head,
 // chunk), four waves.
 //
-//   phase 0  all global loads issued up front: K and V rows into registers, each wave's
-//            Q row tile as MFMA fragments, g and beta
-//   phase 1  K rows and K^T, V^T (token-contiguous) into LDS; wave 0 scans the gates
+//   phase 0  the item's global loads, issued while the previous item is computed: K rows into
+//            registers, each wave's Q row tile as MFMA fragments, g and beta, and one word of
+//            every 128-byte line of the chunk's v rows (see load_kvg)
+//   phase 1  K rows and K^T (token-contiguous) into LDS; wave 0 scans the gates
 //   phase 2  wave 0: Gram tiles of the diagonal blocks and of the first off-diagonal
 //            level, masked into A; unit-lower-triangular 16x16 diagonal inverses by
 //            substitution; first doubling level -- all wave-local.
-//            waves 1..3: their P row tiles (K Q^T on MFMA, masked, stored as permuted
-//            fragments straight from the accumulators), the remaining Gram tiles of A, the
-//            K^T fragments, and zeros above the block diagonal.
-//   phase 3  second doubling level (64-token chunks)
-//   phase 4  W^T = K^T diag(beta Gamma) R^T and Ut = R diag(beta) V on MFMA, stored from the
-//            accumulators (W as permuted fragments, Ut as accumulator tiles)
+//            every wave with a P row tile: that tile (K Q^T on MFMA, masked, kept as permuted
+//            fragments) and, once per key head, its K and Q rows as fragments for the scan;
+//            waves 1..3 also the remaining Gram tiles of A and zeros above the block diagonal.
+//   phase 3  second doubling level (64-token chunks).  Every block of R is also written,
+//            times beta and transposed, to a second LDS array that phase 4 reads
+//   phase 4  Z^T = diag(beta) R^T diag(e) K and P'^T = diag(beta) R^T P^T on MFMA, stored from
+//            the accumulators as permuted fragments of Z and P'
 // A is overwritten in place by R = (I + A)^-1.
 // ------------------------------------------------------------------------------------
-constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // 2^x with the hardware instruction (results below the fp32 normal range flush to zero,
 // which is what the decay factors that use it need)
@@ -186,19 +192,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     constexpr int EPV = 16 / (int)sizeof(E);   // elements per 16-byte vector
     constexpr int LDK = DK + EPV;              // K rows
     constexpr int CP = NKC * KB;               // chunk width padded to whole k-blocks
-    constexpr int LDT = CP + EPV;              // token-contiguous rows (K^T, V^T)
+    constexpr int LDT = CP + EPV;              // token-contiguous rows (K^T)
     constexpr int LDR = CP + 4;                // fp32 A / R rows
-    constexpr int ND = DK / 16, NV = DV / 16;
+    constexpr int ND = DK / 16;
     static_assert(NT == 1 || NT == 2 || NT == 4, "chunk of 16, 32 or 64 tokens");
     constexpr float LOG2E = 1.4426950408889634f;
+    // a k-block of an operand fragment spans the tokens [kb_lo(kb), kb_lo(kb) + KSPAN) (bf16:
+    // 32 consecutive tokens; fp32: four tokens of one 16-token tile, see Elem::kperm)
+    constexpr int KSPAN = KB > 16 ? KB : 16;
+    auto kb_lo = [](int kb) { return kb * KB / KSPAN * KSPAN; };
 
     __shared__ __align__(16) E Ks[C * LDK];
     __shared__ __align__(16) E KsT[DK * LDT];
-    __shared__ __align__(16) E VsT[DV * LDT];
-    __shared__ __align__(16) float sR[C * LDR];   // A, then R in place
-    __shared__ __align__(16) float sg2[C];        // gamma * log2(e)
+    __shared__ __align__(16) float sR[C * LDR];    // A, then R in place
+    __shared__ __align__(16) float sRT[C * LDR];   // row s: beta_s R[r][s] for r < CP (zero past C)
+    __shared__ __align__(16) float sg2[C];         // gamma * log2(e)
     __shared__ __align__(16) float sbeta[CP];
-    __shared__ __align__(16) float sbg[CP];       // beta * Gamma
+    __shared__ __align__(16) float se[CP];         // update scale exp(gamma_last - gamma_r)
     // 1 / |k_r| and 1 / |q_r| of the fused normalisation (NORM only)
     __shared__ __align__(16) float sinvk[NORM ? CP : 4];
     __shared__ __align__(16) float sinvq[NORM ? C : 4];
@@ -235,13 +245,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     };
 
     // ---- loads of an item (rows past the chunk's end read row n - 1 and are zeroed later) ----
-    constexpr int VK = DK / EPV, VV = DV / EPV;
-    constexpr int PK = (C * VK + kThreads - 1) / kThreads, PV = (C * VV + kThreads - 1) / kThreads;
+    constexpr int VK = DK / EPV;
+    constexpr int PK = (C * VK + kThreads - 1) / kThreads;
+    // v: this kernel does not use it, but the scan reads it on its critical path in 32-byte
+    // pieces per row and state slice.  One 4-byte read of each 128-byte line of the chunk's v
+    // rows here brings them into the last-level cache while they are off that path; the words
+    // read are folded into vsink, which only an impossible condition stores.
+    constexpr int LPR = (DV * (int)sizeof(E) + 127) / 128;   // lines per v row
+    constexpr int NVL = (C * LPR + kThreads - 1) / kThreads;
     // this wave's P row tile: wave 0 takes row 0, wave w >= 1 row NT - w (if >= 1)
     const int pm = wave == 0 ? 0 : NT - wave;
     const bool has_prow = wave == 0 || pm >= 1;
     const int pm_ld = max(pm, 0);
-    uint4 kr[PK], vr[PV];
+    uint4 kr[PK];
+    uint32_t vl[NVL];
+    uint32_t vsink = 0;
     frag qf[NKD];
     float graw, braw;
     auto load_kvg = [&](const Item& it) {
@@ -255,9 +273,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             kr[i] = *reinterpret_cast<const uint4*>(kg + (size_t)min(r, n - 1) * rsk + cv * EPV);
         }
 #pragma unroll
-        for (int i = 0; i < PV; ++i) {
-            const int idx = min(tid * PV + i, C * VV - 1), r = idx % C, cv = idx / C;
-            vr[i] = *reinterpret_cast<const uint4*>(vg + (size_t)min(r, n - 1) * rsv + cv * EPV);
+        for (int i = 0; i < NVL; ++i) {
+            const int idx = min(tid + i * kThreads, C * LPR - 1), r = idx / LPR, ln = idx % LPR;
+            vl[i] = *reinterpret_cast<const uint32_t*>(vg + (size_t)min(r, n - 1) * rsv + ln * (128 / (int)sizeof(E)));
         }
         // the gates go to wave 0 alone, which scans them (a token's gates of all heads share a
         // 128-byte line, so each of these loads touches 64 lines)
@@ -291,47 +309,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const bool more = valid(next);
     const Item nxt = decode(more ? next : item);
 
-    // ---- phase 1: K rows, K^T and V^T into LDS; gates -----------------------------------------
-    // rows to Ks; the transposes take each thread's PK consecutive tokens of a column as one
+    // ---- phase 1: K rows and K^T into LDS; gates -----------------------------------------------
+    // rows to Ks; the transpose takes each thread's PK consecutive tokens of a column as one
     // contiguous run per column
-    auto to_lds = [&](const uint4 (&rv)[cmax(PK, PV)], int np, int nvec, E* rows, E* trans) {
-        if (tid * np < nvec) {
-            const int r0 = (tid * np) % C, cv = (tid * np) / C;
-            E el[8][EPV];
+    if (tid * PK < C * VK) {
+        const int r0 = (tid * PK) % C, cv = (tid * PK) / C;
+        E el[PK][EPV];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (i >= np) break;
-                const uint4 z = {0u, 0u, 0u, 0u};
-                const uint4 a = r0 + i < n ? rv[i] : z;
-                if (rows) *reinterpret_cast<uint4*>(rows + (r0 + i) * LDK + cv * EPV) = a;
-                const E* e = reinterpret_cast<const E*>(&a);
+        for (int i = 0; i < PK; ++i) {
+            const uint4 z = {0u, 0u, 0u, 0u};
+            const uint4 a = r0 + i < n ? kr[i] : z;
+            *reinterpret_cast<uint4*>(Ks + (r0 + i) * LDK + cv * EPV) = a;
+            const E* e = reinterpret_cast<const E*>(&a);
 #pragma unroll
-                for (int j = 0; j < EPV; ++j) el[i][j] = e[j];
-            }
-#pragma unroll
-            for (int j = 0; j < EPV; ++j) {
-                E run[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) run[i] = el[i][j];
-                store_run(trans + (cv * EPV + j) * LDT + r0, run, np);
-            }
+            for (int j = 0; j < EPV; ++j) el[i][j] = e[j];
         }
-    };
-    {
-        uint4 kk[cmax(PK, PV)], vv[cmax(PK, PV)];
 #pragma unroll
-        for (int i = 0; i < cmax(PK, PV); ++i) {
-            kk[i] = kr[min(i, PK - 1)];
-            vv[i] = vr[min(i, PV - 1)];
+        for (int j = 0; j < EPV; ++j) {
+            E run[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) run[i] = el[i < PK ? i : 0][j];
+            store_run(KsT + (cv * EPV + j) * LDT + r0, run, PK);
         }
-        to_lds(kk, PK, C * VK, Ks, KsT);
-        to_lds(vv, PV, C * VV, nullptr, VsT);
     }
     if (CP > C) {   // token columns past the chunk (16-token chunks in bf16)
-        for (int e = tid; e < (DK + DV) * (CP - C); e += kThreads) {
+        for (int e = tid; e < DK * (CP - C); e += kThreads) {
             const int d = e / (CP - C), s = C + e % (CP - C);
-            if (d < DK) KsT[d * LDT + s] = X::from_f(0.f);
-            else VsT[(d - DK) * LDT + s] = X::from_f(0.f);
+            KsT[d * LDT + s] = X::from_f(0.f);
         }
     }
     if (wave == 0) {
@@ -347,17 +351,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         if (lane < C) sg2[lane] = x2;
         if (lane < CP) {
             sbeta[lane] = bt;
-            sbg[lane] = bt * exp2f(x2);
+            se[lane] = lane < C ? exp2f(gl2 - x2) : 0.f;   // with NORM: divided by |k_r| below
         }
         if constexpr (!NORM) {   // gate factors for the scan (with NORM: below, scaled)
             float* gf = p.gam + (bh * N + c) * S::GATES;
             if (lane < C) {
                 gf[lane] = exp2f(x2);
-                gf[C + lane] = exp2f(gl2 - x2);
+                gf[C + lane] = exp2f(x2);
             }
             if (lane == 0) gf[2 * C] = exp2f(gl2);
         }
     }
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) vsink ^= vl[i];
     if (more) load_kvg(nxt);   // registers consumed above; the next item's rows are in flight from here
 #pragma unroll
     for (int kb = 0; kb < NKD; ++kb) qf[kb] = X::keep_if(qf[kb], pm_ld * 16 + rl < n);
@@ -404,7 +410,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             if (lane < C) {
                 const float x2 = sg2[lane];
                 gf[lane] = exp2f(x2) * sinvq[lane];
-                gf[C + lane] = exp2f(gl2 - x2) * sinvk[lane];
+                gf[C + lane] = exp2f(x2) * sinvk[lane];
+                se[lane] *= sinvk[lane];
             }
             if (lane == 0) gf[2 * C] = exp2f(gl2);
         }
@@ -433,10 +440,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             sR[r * LDR + s] = (s < r) ? brv[j] * ks * fast_exp2(grv[j] - gs) * G[j] : 0.f;
         }
     };
-    // P row tile m: P[r][s] = exp(gamma_r - gamma_s) (q_r . k_s), s <= r, stored as permuted
-    // A-operand fragments (rows r, k = s) built from tiles D[s][r] = K_t Q_m^T
+    // P row tile m: P[r][s] = exp(gamma_r - gamma_s) (q_r . k_s), s <= r, as permuted A-operand
+    // fragments (rows r, k = s) built from tiles D[s][r] = K_t Q_m^T; kept for phase 4
+    frag pk[NKC];
     auto p_row = [&](int m) {
-        E* Pg = reinterpret_cast<E*>(p.P) + (bh * N + c) * S::P_PER_CHUNK;
         const int r = m * 16 + rl;
         const float gr = sg2[r], qs = NORM ? sinvq[r] : 1.f;
         auto ptile = [&](int t) {
@@ -456,34 +463,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             }
             return acc;
         };
-        // fragments wholly above the diagonal (tokens past row tile m) are never written: the
-        // scan does not read them
         if constexpr (KPL == 8) {
 #pragma unroll
-            for (int kb = 0; kb < NKC; ++kb) {
-                if (2 * kb > m) break;
-                const frag f = X::pack(ptile(2 * kb), 2 * kb + 1 < NT ? ptile(2 * kb + 1) : zero4());
-                *reinterpret_cast<frag*>(Pg + ((size_t)(m * NKC + kb) * 64 + lane) * KPL) = f;
-            }
+            for (int kb = 0; kb < NKC; ++kb)
+                pk[kb] = 2 * kb <= m ? X::pack(ptile(2 * kb), 2 * kb + 1 < NT ? ptile(2 * kb + 1) : zero4()) : X::zero();
         } else {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                if (t > m) break;
                 const f32x4 d = ptile(t);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) Pg[(size_t)(m * NKC + 4 * t + j) * 64 + lane] = X::from_f(d[j]);
+                for (int j = 0; j < 4; ++j) pk[4 * t + j] = d[j];
             }
         }
     };
 
-    // this wave's Q row tile m as fragments for the scan's output products, once per key head
-    // (rows past the chunk are zero)
-    auto store_qf = [&](int m) {
+    // this wave's K and Q row tiles m as fragments for the scan's products with the state,
+    // once per key head (rows past the chunk are zero)
+    auto store_rows = [&](int m) {
         if (h % grp != 0) return;
-        E* QFg = reinterpret_cast<E*>(p.QF) + (((size_t)b * Hk + hk) * N + c) * S::W_PER_CHUNK;
+        const size_t off = (((size_t)b * Hk + hk) * N + c) * S::W_PER_CHUNK;
+        E* KFg = reinterpret_cast<E*>(p.KF) + off;
+        E* QFg = reinterpret_cast<E*>(p.QF) + off;
+        const E* krow = Ks + (m * 16 + rl) * LDK + kq;
 #pragma unroll
-        for (int kb = 0; kb < NKD; ++kb)
-            *reinterpret_cast<frag*>(QFg + ((size_t)(m * NKD + kb) * 64 + lane) * KPL) = qf[kb];
+        for (int kb = 0; kb < NKD; ++kb) {
+            const size_t f = ((size_t)(m * NKD + kb) * 64 + lane) * KPL;
+            *reinterpret_cast<frag*>(KFg + f) = X::ld(krow + kb * KB);
+            *reinterpret_cast<frag*>(QFg + f) = qf[kb];
+        }
     };
 
     // ---- phase 2 -------------------------------------------------------------------------------
@@ -494,7 +501,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int q = 0; q < NT / 2; ++q) G1[q] = kk_tile(2 * q + 1, 2 * q);
         p_row(0);
-        store_qf(0);
+        store_rows(0);
         if (more) load_q(nxt);
 #pragma unroll
         for (int d = 0; d < NT; ++d) mask_a(d, d, Gd[d]);
@@ -525,6 +532,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             wave_lds_sync();
 #pragma unroll
             for (int r = 0; r < 16; ++r) Ab[r * LDR + rl] = x[r];
+            // the same column, times beta, as a row of (R diag(beta))^T
+            float* At = sRT + (g * 16 + rl) * LDR + g * 16;
+            const float bs = sbeta[g * 16 + rl];
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+                *reinterpret_cast<float4*>(At + 4 * r4) =
+                    make_float4(bs * x[4 * r4], bs * x[4 * r4 + 1], bs * x[4 * r4 + 2], bs * x[4 * r4 + 3]);
         }
         wave_lds_sync();
         // first doubling level: R21 = -R22 (A21 R11) for the block pairs (2q, 2q + 1)
@@ -541,11 +555,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             wave_lds_sync();
 #pragma unroll
             for (int j = 0; j < 4; ++j) sR[(hi + rq + j) * LDR + lo + rl] = -r21[j];
+            const float bs = -sbeta[lo + rl];
+            *reinterpret_cast<float4*>(sRT + (lo + rl) * LDR + hi + rq) =
+                make_float4(bs * r21[0], bs * r21[1], bs * r21[2], bs * r21[3]);
         }
     } else {
         if (has_prow) {
             p_row(pm);
-            store_qf(pm);
+            store_rows(pm);
         }
         if (more) load_q(nxt);
         if (NT == 4 && wave >= 2) {   // the 32x32 off-diagonal block, one tile column per wave
@@ -554,29 +571,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             mask_a(2, tn, Ga);
             mask_a(3, tn, Gb);
         }
-        if (h % grp == 0) {   // K^T fragments for the scan, once per key head
-            E* KTg = reinterpret_cast<E*>(p.KT) + (((size_t)b * Hk + hk) * N + c) * S::KT_PER_CHUNK;
-            for (int f = wave - 1; f < ND * NKC; f += 3) {   // tokens in the permuted order
-                const int dt = f / NKC, kb = f % NKC;
-                *reinterpret_cast<frag*>(KTg + ((size_t)f * 64 + lane) * KPL) =
-                    X::ld_perm(KsT + (dt * 16 + rl) * LDT + X::poff(kb, g));
-            }
-        }
-        // zeros above the block diagonal (k-blocks of R read by phase 4 span whole blocks)
+        // the zeros of (R diag(beta))^T: row s, tokens r of earlier 16-token blocks (R is lower
+        // triangular) and past the chunk (phase 4 reads whole rows)
         constexpr int CV = CP / 4;
         for (int e = tid - 64; e < C * CV; e += kThreads - 64) {
-            const int r = e / CV, s4 = (e % CV) * 4;
-            if ((s4 >> 4) > (r >> 4)) *reinterpret_cast<float4*>(sR + r * LDR + s4) = make_float4(0.f, 0.f, 0.f, 0.f);
+            const int s = e / CV, r4 = (e % CV) * 4;
+            if ((r4 >> 4) < (s >> 4) || r4 >= C)
+                *reinterpret_cast<float4*>(sRT + s * LDR + r4) = make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
     lds_barrier();   // (B2)
 
     // ---- phase 3: second doubling level (32x32 blocks) -----------------------------------------
+    // Only (R diag(beta))^T is read after this level, so its block R21 goes there alone.
     if constexpr (NT == 4) {
-        f32x4 t0v = zero4(), t1v = zero4();
-        const int tj = wave;   // tile column of T and R21
         if (wave < 2) {
+            const int tj = wave;   // tile column of T and R21
             // T = A21 R11 (32 x 32, column tile tj); R11 is zero above its diagonal
+            f32x4 t0v = zero4(), t1v = zero4();
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) {
                 if (kb >= 4 * tj) {
@@ -585,9 +597,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                     t1v = mma4(sR[(48 + rl) * LDR + 4 * kb + g], bv, t1v);
                 }
             }
-        }
-        lds_barrier();   // every read of A21 is done before R21 overwrites it
-        if (wave < 2) {
             // R21 = -R22 T; R22 rows 32..47 see T rows 0..15, rows 48..63 all of T
             f32x4 u0 = zero4(), u1 = zero4();
 #pragma unroll
@@ -596,70 +605,99 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 u1 = mma4(sR[(48 + rl) * LDR + 32 + 4 * g + kb], t0v[kb], u1);
                 u1 = mma4(sR[(48 + rl) * LDR + 48 + 4 * g + kb], t1v[kb], u1);
             }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                sR[(32 + rq + j) * LDR + tj * 16 + rl] = -u0[j];
-                sR[(48 + rq + j) * LDR + tj * 16 + rl] = -u1[j];
-            }
+            const float bs = -sbeta[tj * 16 + rl];
+            float* At = sRT + (tj * 16 + rl) * LDR;
+            *reinterpret_cast<float4*>(At + 32 + rq) = make_float4(bs * u0[0], bs * u0[1], bs * u0[2], bs * u0[3]);
+            *reinterpret_cast<float4*>(At + 48 + rq) = make_float4(bs * u1[0], bs * u1[1], bs * u1[2], bs * u1[3]);
         }
         lds_barrier();   // (B3) R complete
     }
 
-    // ---- phase 4: W and Ut -------------------------------------------------------------------
+    // ---- phase 4: Z and P' ------------------------------------------------------------------
+    // Both are stored as permuted A-operand fragments, so each is formed transposed: an
+    // accumulator tile with columns = the operand's rows.  A operands come from rows of sRT.
     {
-        constexpr int WPM = 4 / NT;
-        const int mt = wave % NT, part = wave / NT;
-        const int kbmax = (mt * 16 + 15) / KB;   // k-blocks past it are zero in these rows
-        frag rw[NKC], ru[NKC];
-        const float* rrow = sR + (mt * 16 + rl) * LDR + kq;
+        // Z^T tile (s-tile u, dk-tile dt) = sum over tokens r of (beta_s R[r][s] e_r) K[r][d].
+        // The waves split Z's stored k-blocks: a group is the TPG s-tiles one k-block of Z holds.
+        constexpr int TPG = KPL == 8 ? 2 : 1;
+        constexpr int NG = (NT + TPG - 1) / TPG;
+        const int zg = wave % NG;
+        frag az[TPG][NKC];
 #pragma unroll
-        for (int kb = 0; kb < NKC; ++kb) {
-            rw[kb] = X::zero();
-            ru[kb] = X::zero();
-            if (kb <= kbmax) {
-                float aw[KPL], au[KPL];
+        for (int i = 0; i < TPG; ++i) {
+            const int u = zg * TPG + i;
+            const float* row = sRT + (u * 16 + rl) * LDR;
 #pragma unroll
-                for (int e = 0; e < KPL; ++e) {
-                    const float rv = rrow[kb * KB + e];
-                    aw[e] = rv * sbg[kb * KB + kq + e] * invk(kb * KB + kq + e);
-                    au[e] = rv * sbeta[kb * KB + kq + e];
+            for (int kb = 0; kb < NKC; ++kb) {
+                az[i][kb] = X::zero();
+                if (u < NT && kb_lo(kb) + KSPAN > u * 16) {   // blocks wholly before s-tile u are zero
+                    float t[KPL];
+#pragma unroll
+                    for (int e = 0; e < KPL; ++e) t[e] = row[kb * KB + kq + e] * se[kb * KB + kq + e];
+                    az[i][kb] = X::ld_f(t);
                 }
-                rw[kb] = X::ld_f(aw);
-                ru[kb] = X::ld_f(au);
             }
         }
-        auto wt_tile = [&](int dt) {   // W^T tile: rows dk (tile dt), columns tokens (tile mt)
-            const E* ar = KsT + (dt * 16 + rl) * LDT + kq;
-            f32x4 acc = zero4();
+        E* Zg = reinterpret_cast<E*>(p.Z) + (bh * N + c) * S::Z_PER_CHUNK;
+        for (int dt = wave / NG; dt < ND; dt += 4 / NG) {
+            const E* br = KsT + (dt * 16 + rl) * LDT + kq;
+            f32x4 acc[TPG];
 #pragma unroll
-            for (int kb = 0; kb < NKC; ++kb)
-                if (kb <= kbmax) acc = X::mma(X::ld(ar + kb * KB), rw[kb], acc);
-            return acc;
-        };
-        E* Wg = reinterpret_cast<E*>(p.W) + (bh * N + c) * S::W_PER_CHUNK;
-        if constexpr (KPL == 8) {
-            for (int kbp = part; kbp < NKD; kbp += WPM) {
-                const frag f = X::pack(wt_tile(2 * kbp), wt_tile(2 * kbp + 1));
-                *reinterpret_cast<frag*>(Wg + ((size_t)(mt * NKD + kbp) * 64 + lane) * KPL) = f;
+            for (int i = 0; i < TPG; ++i) acc[i] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < NKC; ++kb) {
+                const frag bk = X::ld(br + kb * KB);
+#pragma unroll
+                for (int i = 0; i < TPG; ++i) {
+                    const int u = zg * TPG + i;
+                    if (u < NT && kb_lo(kb) + KSPAN > u * 16) acc[i] = X::mma(az[i][kb], bk, acc[i]);
+                }
             }
-        } else {
-            for (int dt = part; dt < ND; dt += WPM) {
-                const f32x4 d = wt_tile(dt);
+            if constexpr (KPL == 8) {
+                *reinterpret_cast<frag*>(Zg + ((size_t)(dt * NKC + zg) * 64 + lane) * KPL) = X::pack(acc[0], acc[TPG - 1]);
+            } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) Wg[(size_t)(mt * NKD + 4 * dt + j) * 64 + lane] = X::from_f(d[j]);
+                for (int j = 0; j < 4; ++j) Zg[(size_t)(dt * NKC + 4 * zg + j) * 64 + lane] = acc[0][j];
             }
         }
-        E* Ug = reinterpret_cast<E*>(p.Ut) + (bh * N + c) * S::UT_PER_CHUNK;
-        for (int vt = part; vt < NV; vt += WPM) {
-            const E* br = VsT + (vt * 16 + rl) * LDT + kq;
-            f32x4 acc = zero4();
+
+        // P'^T tile (s-tile u, row tile m) = sum over tokens t of beta_s R[t][s] P[r][t]: the
+        // P fragments kept from phase 2 are the B operand (k = t in the permuted order)
+        if (has_prow) {
+            const int m = pm;
+            f32x4 acc[NT];
 #pragma unroll
-            for (int kb = 0; kb < NKC; ++kb)
-                if (kb <= kbmax) acc = X::mma(ru[kb], X::ld(br + kb * KB), acc);
-            E ov[4];
+            for (int u = 0; u < NT; ++u) {
+                acc[u] = zero4();
+                if (u > m) continue;
+                const float* row = sRT + (u * 16 + rl) * LDR;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ov[j] = X::from_f(acc[j]);
-            store4(Ug + (((size_t)vt * NT + mt) * 64 + lane) * 4, ov);
+                for (int kb = 0; kb < NKC; ++kb) {
+                    if (kb_lo(kb) > m * 16 + 15 || kb_lo(kb) + KSPAN <= u * 16) continue;
+                    float t[KPL];
+#pragma unroll
+                    for (int e = 0; e < KPL; ++e) t[e] = row[X::kperm(kb, g, e)];
+                    acc[u] = X::mma(X::ld_f(t), pk[kb], acc[u]);
+                }
+            }
+            // fragments wholly above the diagonal (tokens past row tile m) are never written:
+            // the scan does not read them
+            E* Pg = reinterpret_cast<E*>(p.P) + (bh * N + c) * S::P_PER_CHUNK;
+            if constexpr (KPL == 8) {
+#pragma unroll
+                for (int kb = 0; kb < NKC; ++kb) {
+                    if (2 * kb > m) break;
+                    *reinterpret_cast<frag*>(Pg + ((size_t)(m * NKC + kb) * 64 + lane) * KPL) =
+                        X::pack(acc[2 * kb], 2 * kb + 1 < NT ? acc[2 * kb + 1] : zero4());
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < NT; ++u) {
+                    if (u > m) break;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) Pg[(size_t)(m * NKC + 4 * u + j) * 64 + lane] = acc[u][j];
+                }
+            }
         }
     }
     if (!more) break;
@@ -667,27 +705,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     item = next;
     cur = nxt;
     }
+    // keeps the v reads above (the value cannot match and T is never negative)
+    if (vsink == 0x9E3779B9u && T < 0) p.gam[0] = 0.f;
 }
 
 // ------------------------------------------------------------------------------------
 // Kernel 2: chunks in order; fp32 state slice in accumulator registers.
 //
-// Eight waves per workgroup in two roles.  Chain waves 0..3 carry the recurrence:
-// U = Ut - W S^T for their 16-token tile, then S^T <- Gamma_n S^T + K^T (e * U) for their
-// state tiles.  Output waves 4..7 compute O = Gamma (Q S^T) + P U for their token tile one
-// barrier behind, from a double-buffered copy of the state, so the output products stay off
-// the chain, and write O as 16-byte pieces staged through LDS.  Each role prefetches its own
+// Eight waves per workgroup in two roles.  Chain waves 0..3 carry the recurrence: the
+// residual Y = V - diag(Gamma) K S^T for their 16-token tile, then S^T <- Gamma_n S^T + Z Y for
+// their state tiles.  Output waves 4..7 compute O = Gamma (Q S^T) + P' Y for their token tile
+// one barrier behind, from a double-buffered copy of the state, so the output products stay
+// off the chain, and write O as 16-byte pieces staged through LDS.  Each role prefetches its own
 // operands NB chunks ahead into registers; the chain waves issue those loads just before the
 // barriers they would wait at anyway, not between a barrier and the next chunk's products.
-// SPLIT: feed the state to W S^T as a bf16 hi + lo pair (two MFMAs) so the delta U sees
+// SPLIT: feed the state to K S^T as a bf16 hi + lo pair (two MFMAs) so the residual Y sees
 // the fp32 state to ~16 bits instead of 8.
 // ------------------------------------------------------------------------------------
 constexpr int kScanThreads = 512;
 // operand sets in flight per wave: chain waves are on the critical path and prefetch
 // deeper; fp32 operands take four times the registers of bf16 ones
 template <typename E> struct ScanDepth;
-template <> struct ScanDepth<bf16_t> { static constexpr int chain = 3, output = 2; };
-template <> struct ScanDepth<float> { static constexpr int chain = 2, output = 1; };
+// (v, read from the caller's array rather than the workspace, arrives later and is fetched
+// further ahead by the chain waves: vrows sets, a multiple of chain)
+template <> struct ScanDepth<bf16_t> { static constexpr int chain = 3, output = 2, vrows = 6; };
+template <> struct ScanDepth<float> { static constexpr int chain = 2, output = 1, vrows = 2; };
 
 template <typename E, int DK, int C, int TPW>
 struct ChainOperands {
@@ -695,11 +737,10 @@ struct ChainOperands {
     typedef typename X::frag frag;
     static constexpr int NKD = DK / X::KB;
     static constexpr int NKC = (C + X::KB - 1) / X::KB;
-    frag w[NKD];
-    frag kt[TPW][NKC];
-    E ut[4];
-    f32x4 e;      // update scale of this lane's four token rows
-    float gn;     // chunk decay exp(gamma_last)
+    frag kf[NKD];       // K row tile (rows tokens, k = dk)
+    frag z[TPW][NKC];   // Z rows of this wave's state tiles (rows dk, k = tokens; permuted)
+    f32x4 gk;           // key-row scale of this lane's four token rows
+    float gn;           // chunk decay exp(gamma_last)
 };
 
 template <typename E, int DK, int C>
@@ -726,14 +767,14 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
     constexpr int CP = NKC * KB;
     constexpr int LDU = CP + EPV;
     constexpr int NSLICE = DV / 16;
-    constexpr int NBC = ScanDepth<E>::chain, NBO = ScanDepth<E>::output;
+    constexpr int NBC = ScanDepth<E>::chain, NBO = ScanDepth<E>::output, NBV = ScanDepth<E>::vrows;
+    static_assert(NBV % NBC == 0, "v sets cycle with the operand sets");
     typedef ChainOperands<E, DK, C, TPW> COps;
     typedef OutputOperands<E, DK, C> OOps;
 
     __shared__ __align__(16) E Sb[2][16 * LDS_];              // state slice, hi part, 2 buffers
     __shared__ __align__(16) E Sl[2][SPLIT ? 16 * LDS_ : EPV];  // lo part
-    __shared__ __align__(16) E UT[16 * LDU];                   // U^T        (for P U)
-    __shared__ __align__(16) E UsT[16 * LDU];                  // (e * U)^T  (for the update)
+    __shared__ __align__(16) E YT[16 * LDU];                   // Y^T (for Z Y and P' Y)
     constexpr int LDO = 16 + EPV;
     __shared__ __align__(16) E Os[4][16 * LDO];                // output tile staging, per output wave
 
@@ -762,29 +803,32 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
     const float* gates = p.gam + (size_t)bh * N * Sh::GATES;   // per chunk: see the workspace layout
 
     for (int e = tid; e < 16 * LDU; e += kScanThreads) {   // columns past the chunk read as zero
-        UT[e] = X::from_f(0.f);
-        UsT[e] = X::from_f(0.f);
+        YT[e] = X::from_f(0.f);
     }
 
     if (chain) {
         // the chain is the critical path: its waves win instruction arbitration on their SIMDs
         __builtin_amdgcn_s_setprio(3);
-        const E* Wg = reinterpret_cast<const E*>(p.W) + (size_t)bh * N * Sh::W_PER_CHUNK;
-        const E* Ug = reinterpret_cast<const E*>(p.Ut) + (size_t)bh * N * Sh::UT_PER_CHUNK;
-        const E* KTg = reinterpret_cast<const E*>(p.KT) + ((size_t)b * Hk + hk) * N * Sh::KT_PER_CHUNK;
+        const E* KFg = reinterpret_cast<const E*>(p.KF) + ((size_t)b * Hk + hk) * N * Sh::W_PER_CHUNK
+                       + ((size_t)m * NKD * 64 + lane) * KPL;
+        const E* Zg = reinterpret_cast<const E*>(p.Z) + (size_t)bh * N * Sh::Z_PER_CHUNK;
+        // v of this lane's state row (i0 + rl) for token rows rq + [0, 4) of tile m
+        const E* vg = reinterpret_cast<const E*>(p.v) + (size_t)h * DV + i0 + rl;
 
-        // the next chunk's operands are fetched in two parts, each issued where this wave
-        // would otherwise wait at a barrier: W, Ut and the update scales once U is formed,
-        // K^T and the decay once the update has read them
+        // a later chunk's operands are fetched in parts, each issued where this wave would
+        // otherwise wait at a barrier: K rows and the key-row scales once Y is formed, Z and the
+        // decay, then v (NBV chunks ahead), once the update has read them
         auto fetch_w = [&](COps& op, int c) {
             const float* gc = gates + (size_t)c * Sh::GATES;
-            op.e = *reinterpret_cast<const f32x4*>(gc + C + m * 16 + rq);
-            const E* wsrc = Wg + (size_t)c * Sh::W_PER_CHUNK + (size_t)m * NKD * Sh::FRAG + lane * KPL;
+            op.gk = *reinterpret_cast<const f32x4*>(gc + C + m * 16 + rq);
+            const E* ksrc = KFg + (size_t)c * Sh::W_PER_CHUNK;
 #pragma unroll
-            for (int kb = 0; kb < NKD; ++kb) op.w[kb] = X::ld(wsrc + kb * Sh::FRAG);
-            const E* usrc = Ug + (size_t)c * Sh::UT_PER_CHUNK + (((size_t)slice * NT + m) * 64 + lane) * 4;
-            if (sizeof(E) == 2) *reinterpret_cast<uint2*>(op.ut) = *reinterpret_cast<const uint2*>(usrc);
-            else *reinterpret_cast<uint4*>(op.ut) = *reinterpret_cast<const uint4*>(usrc);
+            for (int kb = 0; kb < NKD; ++kb) op.kf[kb] = X::ld(ksrc + kb * Sh::FRAG);
+        };
+        auto fetch_v = [&](E (&v)[4], int c) {
+            const int tb = c * C + m * 16 + rq;   // rows past the prompt read its last token
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = vg[((size_t)b * p.Ts + p.t0 + min(tb + j, T - 1)) * Hv * DV];
         };
         auto fetch_k = [&](COps& op, int c) {
             const float* gc = gates + (size_t)c * Sh::GATES;
@@ -792,9 +836,9 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
 #pragma unroll
             for (int tw = 0; tw < TPW; ++tw) {
                 const int dt = min(w4 + 4 * tw, DT - 1);
-                const E* ksrc = KTg + (size_t)c * Sh::KT_PER_CHUNK + ((size_t)dt * NKC * 64 + lane) * KPL;
+                const E* zsrc = Zg + (size_t)c * Sh::Z_PER_CHUNK + ((size_t)dt * NKC * 64 + lane) * KPL;
 #pragma unroll
-                for (int kb = 0; kb < NKC; ++kb) op.kt[tw][kb] = X::ld(ksrc + kb * Sh::FRAG);
+                for (int kb = 0; kb < NKC; ++kb) op.z[tw][kb] = X::ld(zsrc + kb * Sh::FRAG);
             }
         };
         auto fetch = [&](COps& op, int c) { fetch_w(op, c); fetch_k(op, c); };
@@ -827,40 +871,34 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
                 }
             }
         };
-        auto step = [&](COps& op, int c, int nc, auto pftag) {
-            constexpr bool PF = decltype(pftag)::value;
+        auto step = [&](COps& op, E (&v)[4], int c, int nc, int nvc, auto pftag, auto vftag) {
+            constexpr bool PF = decltype(pftag)::value, VF = decltype(vftag)::value;
             // keeps the next step's operand uses (and so their waits) out of this one
             __builtin_amdgcn_sched_barrier(0);
             const int cur = c & 1;
             if (has_tile) {
-                // W fragments hold dk in the permuted order; read S^T to match
-                const E* sr = &Sb[cur][rl * LDS_];
-                const E* sl = &Sl[cur][SPLIT ? rl * LDS_ : 0];
+                const E* sr = &Sb[cur][rl * LDS_ + kq];
+                const E* sl = &Sl[cur][SPLIT ? rl * LDS_ + kq : 0];
                 typename X::frag sh[NKD], slo[NKD];
 #pragma unroll
                 for (int kb = 0; kb < NKD; ++kb) {
-                    sh[kb] = X::ld_perm(sr + X::poff(kb, g));
-                    if (SPLIT) slo[kb] = X::ld_perm(sl + X::poff(kb, g));
+                    sh[kb] = X::ld(sr + kb * KB);
+                    if (SPLIT) slo[kb] = X::ld(sl + kb * KB);
                 }
                 f32x4 acc = zero4(), accl = zero4();
 #pragma unroll
                 for (int kb = 0; kb < NKD; ++kb) {
-                    acc = X::mma(op.w[kb], sh[kb], acc);
-                    if (SPLIT) accl = X::mma(op.w[kb], slo[kb], accl);
+                    acc = X::mma(op.kf[kb], sh[kb], acc);
+                    if (SPLIT) accl = X::mma(op.kf[kb], slo[kb], accl);
                 }
                 if (SPLIT) acc += accl;
-                E u[4], us[4];
+                E y[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float uj = X::to_f(op.ut[j]) - acc[j];
-                    u[j] = X::from_f(uj);
-                    us[j] = X::from_f(uj * op.e[j]);
-                }
-                store4(UT + rl * LDU + m * 16 + rq, u);
-                store4(UsT + rl * LDU + m * 16 + rq, us);
+                for (int j = 0; j < 4; ++j) y[j] = X::from_f(X::to_f(v[j]) - op.gk[j] * acc[j]);
+                store4(YT + rl * LDU + m * 16 + rq, y);
             }
             if (PF) fetch_w(op, nc);
-            lds_barrier();   // (B1) U complete; chunk c's slice was read from buffer cur
+            lds_barrier();   // (B1) Y complete; chunk c's slice was read from buffer cur
 #pragma unroll
             for (int tw = 0; tw < TPW; ++tw) {
                 const int dt = w4 + 4 * tw;
@@ -868,28 +906,40 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
                     f32x4 acc = St[tw] * op.gn;
 #pragma unroll
                     for (int kb = 0; kb < NKC; ++kb)
-                        acc = X::mma(op.kt[tw][kb], X::ld_perm(UsT + rl * LDU + X::poff(kb, g)), acc);
+                        acc = X::mma(op.z[tw][kb], X::ld_perm(YT + rl * LDU + X::poff(kb, g)), acc);
                     St[tw] = acc;
                 }
             }
             if (PF) fetch_k(op, nc);
+            if (VF) fetch_v(v, nvc);
             publish(cur ^ 1);
-            lds_barrier();   // (B2) next slice published; output waves are done with U
+            lds_barrier();   // (B2) next slice published; output waves are done with Y
         };
 
         publish(0);
         COps op[NBC];
+        E vb[NBV][4];
 #pragma unroll
         for (int j = 0; j < NBC; ++j) fetch(op[j], min(j, N - 1));
+#pragma unroll
+        for (int j = 0; j < NBV; ++j) fetch_v(vb[j], min(j, N - 1));
         lds_barrier();
+        std::true_type yes;
+        std::false_type no;
         int c = 0;
-        for (; c + NBC <= N; c += NBC) {
+        for (; c + NBV <= N; c += NBV) {
 #pragma unroll
-            for (int j = 0; j < NBC; ++j) step(op[j], c + j, min(c + j + NBC, N - 1), std::true_type{});
+            for (int j = 0; j < NBV; ++j)
+                step(op[j % NBC], vb[j], c + j, min(c + j + NBC, N - 1), min(c + j + NBV, N - 1), yes, yes);
         }
+        // fewer than NBV chunks left: the v sets hold all of them, the operand sets the next
+        // NBC and are refilled while chunks remain
 #pragma unroll
-        for (int j = 0; j < NBC; ++j)
-            if (c + j < N) step(op[j], c + j, 0, std::false_type{});
+        for (int j = 0; j < NBV; ++j) {
+            if (c + j >= N) break;
+            if (c + j + NBC < N) step(op[j % NBC], vb[j], c + j, c + j + NBC, 0, yes, no);
+            else step(op[j % NBC], vb[j], c + j, 0, 0, no, no);
+        }
 
 #pragma unroll
         for (int tw = 0; tw < TPW; ++tw) {
@@ -922,7 +972,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
             constexpr bool TAIL = decltype(tailtag)::value;
             __builtin_amdgcn_sched_barrier(0);
             const int t0 = c * C;
-            lds_barrier();   // (B1) U of chunk c is in LDS; buffer (c & 1) holds chunk c's slice
+            lds_barrier();   // (B1) Y of chunk c is in LDS; buffer (c & 1) holds chunk c's slice
             if (has_tile) {
                 const E* sr = &Sb[c & 1][rl * LDS_ + kq];
                 const bool qok = !TAIL || (t0 + m * 16 + rl < T);
@@ -933,7 +983,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
                 f32x4 acc = accq * op.gr;
 #pragma unroll
                 for (int kb = 0; kb < NKC; ++kb)   // P fragments: tokens in the permuted order
-                    if (kb <= pkmax) acc = X::mma(op.p[kb], X::ld_perm(UT + rl * LDU + X::poff(kb, g)), acc);
+                    if (kb <= pkmax) acc = X::mma(op.p[kb], X::ld_perm(YT + rl * LDU + X::poff(kb, g)), acc);
                 // O tile through LDS, written as 16-byte pieces (a token's 16 state rows are
                 // sizeof(E) pieces)
                 E* os = Os[w4];

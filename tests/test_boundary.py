@@ -38,9 +38,9 @@ def test_abi_version_and_status_strings():
 
 def test_workspace_bytes():
     # prefill at T=4096, Hk=16, Hv=32, dk=dv=128, chunk 64, bf16:
-    # W, Ut: 32*4096*128*2 each; P: 32*4096*64*2; K^T and the q fragments: 16*4096*128*2 each;
-    # gate factors: 32 heads * 64 chunks * (2*64 + 4) floats
-    expect = 2 * 32 * 4096 * 128 * 2 + 32 * 4096 * 64 * 2 + 2 * 16 * 4096 * 128 * 2 + 32 * 64 * 132 * 4
+    # k and q fragments: 16*4096*128*2 each; Z: 32 heads * 64 chunks * 128*64*2;
+    # P': 32*4096*64*2; gate factors: 32 heads * 64 chunks * (2*64 + 4) floats
+    expect = 2 * 16 * 4096 * 128 * 2 + 32 * 64 * 128 * 64 * 2 + 32 * 4096 * 64 * 2 + 32 * 64 * 132 * 4
     assert gdn.gdn_prefill_workspace_bytes(1, 4096, 16, 32, 128, 128, 64, 0) == expect
     assert gdn.gdn_prefill_workspace_bytes(1, 0, 16, 32, 128, 128, 64, 0) == 0
     assert gdn.gdn_prefill_workspace_bytes(1, 64, 16, 32, 96, 128, 64, 0) == 0     # unsupported
