@@ -153,7 +153,7 @@ __device__ __forceinline__ void store_run(E* dst, const E (&v)[8], int np) {
 //
 //   phase 0  the item's global loads, issued while the previous item is computed: K rows into
 //            registers, each wave's Q row tile as MFMA fragments, g and beta, and one word of
-//            every 128-byte line of the chunk's v rows (see load_kvg)
+//            every 128-byte line of the chunk's v rows (see touch_v)
 //   phase 1  K rows and K^T (token-contiguous) into LDS; wave 0 scans the gates
 //   phase 2  wave 0: Gram tiles of the diagonal blocks and of the first off-diagonal
 //            level, masked into A; unit-lower-triangular 16x16 diagonal inverses by
@@ -249,33 +249,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     constexpr int PK = (C * VK + kThreads - 1) / kThreads;
     // v: this kernel does not use it, but the scan reads it on its critical path in 32-byte
     // pieces per row and state slice.  One 4-byte read of each 128-byte line of the chunk's v
-    // rows here brings them into the last-level cache while they are off that path; the words
-    // read are folded into vsink, which only an impossible condition stores.
+    // rows here (by waves 1..3, after the next item's other loads) brings them into the
+    // last-level cache while they are off that path; the words read are folded into vsink,
+    // which only an impossible condition stores.
     constexpr int LPR = (DV * (int)sizeof(E) + 127) / 128;   // lines per v row
-    constexpr int NVL = (C * LPR + kThreads - 1) / kThreads;
+    constexpr int NVL = (C * LPR + kThreads - 65) / (kThreads - 64);
     // this wave's P row tile: wave 0 takes row 0, wave w >= 1 row NT - w (if >= 1)
     const int pm = wave == 0 ? 0 : NT - wave;
     const bool has_prow = wave == 0 || pm >= 1;
     const int pm_ld = max(pm, 0);
     uint4 kr[PK];
-    uint32_t vl[NVL];
+    uint32_t vl[NVL] = {};
     uint32_t vsink = 0;
     frag qf[NKD];
     float graw, braw;
-    auto load_kvg = [&](const Item& it) {
+    auto load_kg = [&](const Item& it) {
         const int t0 = it.c * C, n = min(C, T - t0);
         const E* kg = reinterpret_cast<const E*>(p.k) + ((size_t)it.b * p.Ts + p.t0 + t0) * rsk + (size_t)(it.h / grp) * DK;
-        const E* vg = reinterpret_cast<const E*>(p.v) + ((size_t)it.b * p.Ts + p.t0 + t0) * rsv + (size_t)it.h * DV;
         // thread tid holds vectors tid * PK + [0, PK): PK consecutive tokens of one column block
 #pragma unroll
         for (int i = 0; i < PK; ++i) {
             const int idx = min(tid * PK + i, C * VK - 1), r = idx % C, cv = idx / C;
             kr[i] = *reinterpret_cast<const uint4*>(kg + (size_t)min(r, n - 1) * rsk + cv * EPV);
-        }
-#pragma unroll
-        for (int i = 0; i < NVL; ++i) {
-            const int idx = min(tid + i * kThreads, C * LPR - 1), r = idx / LPR, ln = idx % LPR;
-            vl[i] = *reinterpret_cast<const uint32_t*>(vg + (size_t)min(r, n - 1) * rsv + ln * (128 / (int)sizeof(E)));
         }
         // the gates go to wave 0 alone, which scans them (a token's gates of all heads share a
         // 128-byte line, so each of these loads touches 64 lines)
@@ -283,6 +278,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             const size_t gidx = ((size_t)it.b * p.Ts + p.t0 + t0 + min(lane, n - 1)) * Hv + it.h;
             graw = p.g[gidx];
             braw = p.beta[gidx];
+        }
+    };
+    auto touch_v = [&](const Item& it) {   // waves 1..3
+        const int t0 = it.c * C, n = min(C, T - t0);
+        const E* vg = reinterpret_cast<const E*>(p.v) + ((size_t)it.b * p.Ts + p.t0 + t0) * rsv + (size_t)it.h * DV;
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) {
+            const int idx = min(tid - 64 + i * (kThreads - 64), C * LPR - 1), r = idx / LPR, ln = idx % LPR;
+            vl[i] = *reinterpret_cast<const uint32_t*>(vg + (size_t)min(r, n - 1) * rsv + ln * (128 / (int)sizeof(E)));
         }
     };
     auto load_q = [&](const Item& it) {
@@ -296,8 +300,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     int item = blockIdx.x;
     if (!valid(item)) return;
     Item cur = decode(item);
-    load_kvg(cur);
+    load_kg(cur);
     load_q(cur);
+    if (wave > 0) touch_v(cur);
     for (;;) {
     const int c = cur.c, h = cur.h, b = cur.b;
     const int hk = h / grp;
@@ -364,7 +369,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
 #pragma unroll
     for (int i = 0; i < NVL; ++i) vsink ^= vl[i];
-    if (more) load_kvg(nxt);   // registers consumed above; the next item's rows are in flight from here
+    if (more) load_kg(nxt);   // registers consumed above; the next item's rows are in flight from here
 #pragma unroll
     for (int kb = 0; kb < NKD; ++kb) qf[kb] = X::keep_if(qf[kb], pm_ld * 16 + rl < n);
     lds_barrier();   // (B1)
@@ -564,7 +569,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             p_row(pm);
             store_rows(pm);
         }
-        if (more) load_q(nxt);
+        if (more) {
+            load_q(nxt);
+            touch_v(nxt);
+        }
         if (NT == 4 && wave >= 2) {   // the 32x32 off-diagonal block, one tile column per wave
             const int tn = wave - 2;
             const f32x4 Ga = kk_tile(2, tn), Gb = kk_tile(3, tn);
@@ -926,19 +934,12 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
         lds_barrier();
         std::true_type yes;
         std::false_type no;
-        int c = 0;
-        for (; c + NBV <= N; c += NBV) {
+        // one loop over all chunks, NBV per pass (the last pass skips the steps past N and the
+        // last prefetches repeat chunk N - 1), so no set lives across a separate tail
+        for (int c = 0; c < N; c += NBV) {
 #pragma unroll
             for (int j = 0; j < NBV; ++j)
-                step(op[j % NBC], vb[j], c + j, min(c + j + NBC, N - 1), min(c + j + NBV, N - 1), yes, yes);
-        }
-        // fewer than NBV chunks left: the v sets hold all of them, the operand sets the next
-        // NBC and are refilled while chunks remain
-#pragma unroll
-        for (int j = 0; j < NBV; ++j) {
-            if (c + j >= N) break;
-            if (c + j + NBC < N) step(op[j % NBC], vb[j], c + j, c + j + NBC, 0, yes, no);
-            else step(op[j % NBC], vb[j], c + j, 0, 0, no, no);
+                if (c + j < N) step(op[j % NBC], vb[j], c + j, min(c + j + NBC, N - 1), min(c + j + NBV, N - 1), yes, yes);
         }
 
 #pragma unroll
