@@ -42,9 +42,10 @@ CPU_BASELINE_S = 10.0           # seconds of oracle work timed for the CPU basel
 # bf16 each), v and o (32 heads x 128 x bf16 each), g and beta (32 heads x fp32 each).
 PREFILL_BYTES_PER_TOKEN = 16 * 128 * 2 * 2 + 32 * 128 * 2 * 2 + 32 * 4 * 2     # 24,832
 STATE_BYTES = 32 * 128 * 128 * 4                                               # 2 MiB
-# Matrix-core FLOPs of the blockwise form per token per value head (chunk C = 64, dk = dv = 128,
-# the two Gram blocks shared by the two value heads of a key head):
+# Matrix-core FLOPs of the pages' blockwise form per token per value head (chunk C = 64,
+# dk = dv = 128, the two Gram blocks shared by the two value heads of a key head):
 #   2 * [C dk (Grams) + C dk (W) + 2 C dv (U~, P U) + 3 dk dv (W S^T, Q S^T, U^T K) + C^2 / 6 (inverse)]
+# (the residual form the kernels use does about 8% fewer: no U~ product, P R diag(beta) added)
 PREFILL_FLOP_PER_TOKEN_HEAD = 2 * (64 * 128 + 64 * 128 + 2 * 64 * 128 + 3 * 128 * 128 + 64 * 64 / 6)
 # Decode: each fp32 state element read once and written once, plus q, k, v, g, beta, o.
 DECODE_BYTES_PER_LAYER = 2 * STATE_BYTES + PREFILL_BYTES_PER_TOKEN                  # 4,219,136
