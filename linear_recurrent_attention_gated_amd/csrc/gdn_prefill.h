@@ -927,19 +927,56 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
         publish(0);
         COps op[NBC];
         E vb[NBV][4];
+        // first fetches in the order the loop issues them (each operand set followed by the v
+        // set NBV - NBC later), so that the outstanding loads stand in the same order when the
+        // loop is entered as when it repeats, and the waits at its head stay exact
+        // (the scheduling barriers keep the compiler from regrouping them)
+        auto prologue = [&] {
 #pragma unroll
-        for (int j = 0; j < NBC; ++j) fetch(op[j], min(j, N - 1));
+            for (int j = 0; j < NBV - NBC; ++j) {
+                fetch_v(vb[j], min(j, N - 1));
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
-        for (int j = 0; j < NBV; ++j) fetch_v(vb[j], min(j, N - 1));
-        lds_barrier();
+            for (int j = 0; j < NBC; ++j) {
+                fetch_w(op[j], min(j, N - 1));
+                __builtin_amdgcn_sched_barrier(0);
+                fetch_k(op[j], min(j, N - 1));
+                __builtin_amdgcn_sched_barrier(0);
+                fetch_v(vb[NBV - NBC + j], min(NBV - NBC + j, N - 1));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            lds_barrier();
+        };
+        // the last chunks after c, fewer than NBV: the v sets hold all of them, the operand sets
+        // the next NBC, refilled while chunks remain
         std::true_type yes;
         std::false_type no;
-        // one loop over all chunks, NBV per pass (the last pass skips the steps past N and the
-        // last prefetches repeat chunk N - 1), so no set lives across a separate tail
-        for (int c = 0; c < N; c += NBV) {
+        auto remainder = [&](int c) {
 #pragma unroll
-            for (int j = 0; j < NBV; ++j)
-                if (c + j < N) step(op[j % NBC], vb[j], c + j, min(c + j + NBC, N - 1), min(c + j + NBV, N - 1), yes, yes);
+            for (int j = 0; j < NBV; ++j) {
+                if (c + j >= N) break;
+                if (c + j + NBC < N) step(op[j % NBC], vb[j], c + j, c + j + NBC, 0, yes, no);
+                else step(op[j % NBC], vb[j], c + j, 0, 0, no, no);
+            }
+        };
+        // The loop runs whole passes of NBV chunks only: a pass that could stop part-way would
+        // let the waits at the loop's head assume the last loads of a cut-short pass are the
+        // newest.  Prompts shorter than one pass take a separate path, so that no operand set
+        // has to live across the loop into the remainder (which made the compiler spill them).
+        if (N >= NBV) {
+            prologue();
+            int c = 0;
+            do {
+#pragma unroll
+                for (int j = 0; j < NBV; ++j)
+                    step(op[j % NBC], vb[j], c + j, min(c + j + NBC, N - 1), min(c + j + NBV, N - 1), yes, yes);
+                c += NBV;
+            } while (c + NBV <= N);
+            remainder(c);
+        } else {
+            prologue();
+            remainder(0);
         }
 
 #pragma unroll
