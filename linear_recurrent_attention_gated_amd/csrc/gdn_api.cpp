@@ -27,7 +27,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Longest prompt for which GDN_PATH_AUTO takes the token-sequential path: measured crossover
 // of the two prefill forms on MI355X at 16 key / 32 value heads, dk = dv = 128, bf16.
-constexpr int kSequentialMaxTokens = 56;
+constexpr int kSequentialMaxTokens = 44;
 
 // Workspace regions of the blockwise prefill (see gdn_prefill.h).
 struct Layout {

@@ -734,9 +734,9 @@ constexpr int kScanThreads = 512;
 // operand sets in flight per wave: chain waves are on the critical path and prefetch
 // deeper; fp32 operands take four times the registers of bf16 ones
 template <typename E> struct ScanDepth;
-// (v, read from the caller's array rather than the workspace, arrives later and is fetched
-// further ahead by the chain waves: vrows sets, a multiple of chain)
-template <> struct ScanDepth<bf16_t> { static constexpr int chain = 3, output = 2, vrows = 6; };
+// (v, read from the caller's array rather than the workspace, is held in sets of its own:
+// vrows, a multiple of chain; fetching it 6 chunks ahead instead of 3 measured no faster)
+template <> struct ScanDepth<bf16_t> { static constexpr int chain = 3, output = 2, vrows = 3; };
 template <> struct ScanDepth<float> { static constexpr int chain = 2, output = 1, vrows = 2; };
 
 template <typename E, int DK, int C, int TPW>
