@@ -209,14 +209,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     __shared__ __align__(16) float sg2[C];         // gamma * log2(e)
     __shared__ __align__(16) float sbeta[CP];
     __shared__ __align__(16) float se[CP];         // update scale exp(gamma_last - gamma_r)
-    // 1 / |k_r| and 1 / |q_r| of the fused normalisation (NORM only)
-    __shared__ __align__(16) float sinvk[NORM ? CP : 4];
-    __shared__ __align__(16) float sinvq[NORM ? C : 4];
-    auto invk = [&](int r) { return NORM ? sinvk[r] : 1.f; };
-    auto invk4 = [&](int r) {
-        if constexpr (NORM) return *reinterpret_cast<const float4*>(sinvk + r);
-        return make_float4(1.f, 1.f, 1.f, 1.f);
-    };
+    // fused normalisation (NORM only): |k_r|^2 in parts, one per 16-byte column block of the
+    // rows (written where the rows are stored to LDS), and 1 / |k_r| formed from them by every
+    // wave into its own copy, so that no barrier is spent on it
+    constexpr int VKN = DK / EPV;   // column blocks of a K row
+    __shared__ __align__(16) float sk2p[NORM ? C * (VKN + 1) : 4];
+    __shared__ __align__(16) float sinvk[NORM ? 4 * CP : 4];
 
     const int T = p.T, Hk = p.Hk, Hv = p.Hv, N = p.N;
     const int grp = Hv / Hk;
@@ -224,6 +222,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rl = lane & 15, g = lane >> 4, kq = g * KPL, rq = g * 4;
     const size_t rsk = (size_t)Hk * DK, rsv = (size_t)Hv * DV;
+    const float* winvk = sinvk + (NORM ? wave * CP : 0);
+    auto invk = [&](int r) { return NORM ? winvk[r] : 1.f; };
+    auto invk4 = [&](int r) {
+        if constexpr (NORM) return *reinterpret_cast<const float4*>(winvk + r);
+        return make_float4(1.f, 1.f, 1.f, 1.f);
+    };
+    float invq = 1.f;   // 1 / |q_r| of this lane's row of the wave's P row tile (NORM)
 
     // Work items are (batch, chunk, value head).  Item i takes value head (i / 8) % grp of
     // "rest" (i / (8 grp)) * 8 + i % 8, which names (batch, chunk, key head): with a grid that
@@ -328,6 +333,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             const E* e = reinterpret_cast<const E*>(&a);
 #pragma unroll
             for (int j = 0; j < EPV; ++j) el[i][j] = e[j];
+            if constexpr (NORM) {
+                float ss = 0.f;
+#pragma unroll
+                for (int j = 0; j < EPV; ++j) {
+                    const float x = X::to_f(e[j]);
+                    ss += x * x;
+                }
+                sk2p[(r0 + i) * (VKN + 1) + cv] = ss;
+            }
         }
 #pragma unroll
         for (int j = 0; j < EPV; ++j) {
@@ -356,9 +370,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         if (lane < C) sg2[lane] = x2;
         if (lane < CP) {
             sbeta[lane] = bt;
-            se[lane] = lane < C ? exp2f(gl2 - x2) : 0.f;   // with NORM: divided by |k_r| below
+            se[lane] = lane < C ? exp2f(gl2 - x2) : 0.f;   // with NORM: divided by |k_r| in phase 2
         }
-        if constexpr (!NORM) {   // gate factors for the scan (with NORM: below, scaled)
+        if constexpr (!NORM) {   // gate factors for the scan (with NORM: in phase 2, scaled)
             float* gf = p.gam + (bh * N + c) * S::GATES;
             if (lane < C) {
                 gf[lane] = exp2f(x2);
@@ -374,27 +388,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int kb = 0; kb < NKD; ++kb) qf[kb] = X::keep_if(qf[kb], pm_ld * 16 + rl < n);
     lds_barrier();   // (B1)
     if constexpr (NORM) {
-        // 1 / |k_r| from the K rows in LDS (four threads per row), 1 / |q_r| from each wave's
-        // Q row tile (lane groups hold a quarter of a row each); rows past the chunk are zero
-        constexpr int QPR = DK / 4;
-        if (tid < 4 * C) {
-            const int r = tid / 4, part = tid % 4;
+        // 1 / |k_r| into this wave's copy (lane r sums row r's parts; rows past the chunk are
+        // zero), 1 / |q_r| from the wave's Q row tile (lane groups hold a quarter of a row each)
+        float* w = sinvk + wave * CP;
+        if (lane < C) {
             float ss = 0.f;
 #pragma unroll
-            for (int v = 0; v < QPR / EPV; ++v) {
-                const uint4 u = *reinterpret_cast<const uint4*>(Ks + r * LDK + part * QPR + v * EPV);
-                const E* e = reinterpret_cast<const E*>(&u);
-#pragma unroll
-                for (int j = 0; j < EPV; ++j) {
-                    const float x = X::to_f(e[j]);
-                    ss += x * x;
-                }
-            }
-            ss += __shfl_xor(ss, 1, 64);
-            ss += __shfl_xor(ss, 2, 64);
-            if (part == 0) sinvk[r] = rsqrtf(ss + kNormEps);
+            for (int v = 0; v < VKN; ++v) ss += sk2p[lane * (VKN + 1) + v];
+            w[lane] = rsqrtf(ss + kNormEps);
+        } else if (lane < CP) {
+            w[lane] = 1.f;
         }
-        if (tid < CP - C) sinvk[C + tid] = 1.f;
         if (has_prow) {
             float ss = 0.f;
 #pragma unroll
@@ -406,21 +410,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 }
             ss += __shfl_xor(ss, 16, 64);
             ss += __shfl_xor(ss, 32, 64);
-            if (g == 0) sinvq[pm * 16 + rl] = rsqrtf(ss + kNormEps);
+            invq = rsqrtf(ss + kNormEps);
         }
-        lds_barrier();
-        if (wave == 0) {
-            float* gf = p.gam + (bh * N + c) * S::GATES;
-            const float gl2 = sg2[C - 1];
-            if (lane < C) {
-                const float x2 = sg2[lane];
-                gf[lane] = exp2f(x2) * sinvq[lane];
-                gf[C + lane] = exp2f(x2) * sinvk[lane];
-                se[lane] *= sinvk[lane];
-            }
-            if (lane == 0) gf[2 * C] = exp2f(gl2);
-        }
+        wave_lds_sync();
     }
+    // with NORM, the gate factors of this wave's P rows, scaled by the norms (before the end of
+    // phase 2: phase 4 reads se)
+    auto norm_gates = [&] {
+        if constexpr (NORM) {
+            float* gf = p.gam + (bh * N + c) * S::GATES;
+            if (has_prow && g == 0) {
+                const int r = pm * 16 + rl;
+                const float gr = exp2f(sg2[r]), ik = invk(r);
+                gf[r] = gr * invq;
+                gf[C + r] = gr * ik;
+                se[r] *= ik;
+            }
+            if (wave == 0 && lane == 0) gf[2 * C] = exp2f(sg2[C - 1]);
+        }
+    };
 
     // Gram tile of K rows: D[r][s] = k_r . k_s  (r in tile tm, s in tile tn)
     auto kk_tile = [&](int tm, int tn) {
@@ -450,7 +458,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     frag pk[NKC];
     auto p_row = [&](int m) {
         const int r = m * 16 + rl;
-        const float gr = sg2[r], qs = NORM ? sinvq[r] : 1.f;
+        const float gr = sg2[r], qs = invq;   // (this wave's own row tile)
         auto ptile = [&](int t) {
             f32x4 acc = zero4();
             if (t <= m) {
@@ -588,6 +596,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 *reinterpret_cast<float4*>(sRT + s * LDR + r4) = make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
+    norm_gates();
     lds_barrier();   // (B2)
 
     // ---- phase 3: second doubling level (32x32 blocks) -----------------------------------------
