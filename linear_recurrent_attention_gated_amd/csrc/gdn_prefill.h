@@ -643,7 +643,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int i = 0; i < TPG; ++i) {
             const int u = zg * TPG + i;
-            const float* row = sRT + (u * 16 + rl) * LDR;
+            const float* row = sRT + (min(u, NT - 1) * 16 + rl) * LDR;   // (s-tiles past the chunk: unused)
 #pragma unroll
             for (int kb = 0; kb < NKC; ++kb) {
                 az[i][kb] = X::zero();

@@ -56,6 +56,7 @@ CASES = [
     (1, 150, 1, 4, 64, 64, 64, True),
     (2, 77, 2, 8, 128, 64, 32, True),
     (8, 40, 1, 4, 32, 32, 16, True),
+    (1, 80, 1, 2, 128, 128, 16, True),
 ]
 
 
