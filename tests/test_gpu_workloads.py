@@ -234,6 +234,36 @@ def test_segmented_prefill_equals_one_pass(dt, chunk, seg_chunks):
     assert nrel(np32(o2), o_ref) < TOL_O and nrel(s2.cpu().numpy(), s_ref) < TOL_S
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_prepare_then_scan_equals_one_call(dt):
+    # gdn_prefill is gdn_prefill_prepare followed by gdn_prefill_scan on one workspace: the two
+    # stages called separately (the scan also reads v itself) give the same bits, also when
+    # another call's stages ran on a second workspace in between
+    d = make_inputs(1, 300, 2, 4, 128, 128, seed=41, state_std=0.1, dtype=dt)
+    e = make_inputs(1, 300, 2, 4, 128, 128, seed=42, state_std=0.1, dtype=dt)
+    dd, de = to_dev(d), to_dev(e)
+    nbytes = gdn.gdn_prefill_workspace_bytes(1, 300, 2, 4, 128, 128, 64, dt)
+    ws1 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    st = torch.as_tensor(np.asarray(d["state"], np.float32)).cuda()
+    ste = torch.as_tensor(np.asarray(e["state"], np.float32)).cuda()
+    o1 = torch.empty_like(dd["v"])
+    s1 = torch.empty((1, 4, 128, 128), dtype=torch.float32, device="cuda")
+    o2, s2 = torch.empty_like(o1), torch.empty_like(s1)
+    oe, se = torch.empty_like(o1), torch.empty_like(s1)
+    say("prepare+scan", dt)
+    args = (dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], st)
+    gdn.gdn_prefill(*args, o1, s1, 64, ws1)
+    gdn.gdn_prefill_prepare(*args, o2, s2, 64, ws1)
+    gdn.gdn_prefill_prepare(de["q"], de["k"], de["v"], de["g"], de["beta"], ste, oe, se, 64, ws2)
+    gdn.gdn_prefill_scan(de["q"], de["k"], de["v"], de["g"], de["beta"], ste, oe, se, 64, ws2)
+    gdn.gdn_prefill_scan(*args, o2, s2, 64, ws1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    o_ref, s_ref = oracle_prefill(e, e["state"])
+    assert nrel(np32(oe), o_ref) < TOL_O and nrel(se.cpu().numpy(), s_ref) < TOL_S
+
+
 def test_long_128k_bounded_workspace(c4):
     # the 131072-token prompt with a 256 MiB workspace (the one-pass workspace is ~3 GiB)
     d, o_full, s_full = c4
