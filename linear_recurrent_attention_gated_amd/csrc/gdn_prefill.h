@@ -832,9 +832,10 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
         // v of this lane's state row (i0 + rl) for token rows rq + [0, 4) of tile m
         const E* vg = reinterpret_cast<const E*>(p.v) + (size_t)h * DV + i0 + rl;
 
-        // a later chunk's operands are fetched in parts, each issued where this wave would
-        // otherwise wait at a barrier: K rows and the key-row scales once Y is formed, Z and the
-        // decay, then v (NBV chunks ahead), once the update has read them
+        // a later chunk's operands are fetched in parts, each issued where its registers are
+        // free and this wave would otherwise wait: K rows and the key-row scales once Y is
+        // formed (before the first barrier), v (NBV chunks ahead) right after that barrier, Z
+        // and the decay once the update has read them (before the second)
         auto fetch_w = [&](COps& op, int c) {
             const float* gc = gates + (size_t)c * Sh::GATES;
             op.gk = *reinterpret_cast<const f32x4*>(gc + C + m * 16 + rq);
@@ -916,6 +917,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
             }
             if (PF) fetch_w(op, nc);
             lds_barrier();   // (B1) Y complete; chunk c's slice was read from buffer cur
+            if (VF) fetch_v(v, nvc);
 #pragma unroll
             for (int tw = 0; tw < TPW; ++tw) {
                 const int dt = w4 + 4 * tw;
@@ -928,7 +930,6 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
                 }
             }
             if (PF) fetch_k(op, nc);
-            if (VF) fetch_v(v, nvc);
             publish(cur ^ 1);
             lds_barrier();   // (B2) next slice published; output waves are done with Y
         };
@@ -936,8 +937,8 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
         publish(0);
         COps op[NBC];
         E vb[NBV][4];
-        // first fetches in the order the loop issues them (each operand set followed by the v
-        // set NBV - NBC later), so that the outstanding loads stand in the same order when the
+        // first fetches in the order the loop issues them (each operand set's K rows, then the v
+        // set NBV - NBC later, then the set's Z), so that the outstanding loads stand in the same order when the
         // loop is entered as when it repeats, and the waits at its head stay exact
         // (the scheduling barriers keep the compiler from regrouping them)
         auto prologue = [&] {
@@ -950,9 +951,9 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
             for (int j = 0; j < NBC; ++j) {
                 fetch_w(op[j], min(j, N - 1));
                 __builtin_amdgcn_sched_barrier(0);
-                fetch_k(op[j], min(j, N - 1));
-                __builtin_amdgcn_sched_barrier(0);
                 fetch_v(vb[NBV - NBC + j], min(NBV - NBC + j, N - 1));
+                __builtin_amdgcn_sched_barrier(0);
+                fetch_k(op[j], min(j, N - 1));
                 __builtin_amdgcn_sched_barrier(0);
             }
             lds_barrier();
