@@ -495,6 +495,10 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": pf_bytes,
+            "algorithmic_bytes_note": "q, k, v, g, beta read and o, state_out written once "
+                                      "(24,832 B/token + 2 MiB); the zero start state is passed "
+                                      "as NULL, so no state_in read is counted (a nonzero "
+                                      "state_in adds 2 MiB)",
             "achievable_copy_gbs": round(copy_gbs, 1),
             "frac_of_copy": round(achieved / copy_gbs, 4),
         },
@@ -516,24 +520,37 @@ def main():
     }
 
     if not args.no_cpu_baseline:
+        # The oracle and the GPU prefill alternate within each round, in alternating order
+        # (GPU then oracle in even rounds, oracle then GPU in odd ones), until about
+        # CPU_BASELINE_S seconds of oracle work are done: background load and clock drift then
+        # bias neither leg.
         from oracle import gdn_oracle as orc
         try:
             ncpu = len(os.sched_getaffinity(0))
         except AttributeError:
             ncpu = os.cpu_count() or 1
-        threads = args.cpu_threads or max(1, min(16, ncpu))
+        threads = args.cpu_threads or ncpu
         f = lambda t: t.float().numpy()  # noqa: E731
         qa, ka, va, ga, ba = (f(host[k]) for k in ("q", "k", "v", "g", "beta"))
-        # the whole workload, repeated until about CPU_BASELINE_S seconds have passed
-        reps = 0
-        c0 = time.perf_counter()
-        while True:
-            o_ref, s_ref = orc.seq(qa, ka, va, ga, ba, nthreads=threads, rows_per_item=8)
-            reps += 1
-            if time.perf_counter() - c0 >= CPU_BASELINE_S:
-                break
-        cpu_total = time.perf_counter() - c0
-        cpu_s = cpu_total / reps
+        cpu_runs, gpu_alt = [], []
+        r = 0
+        while sum(cpu_runs) < CPU_BASELINE_S or r < 2:
+            legs = ("gpu", "cpu") if r % 2 == 0 else ("cpu", "gpu")
+            for leg in legs:
+                if leg == "cpu":
+                    c0 = time.perf_counter()
+                    o_ref, s_ref = orc.seq(qa, ka, va, ga, ba, nthreads=threads, rows_per_item=8)
+                    cpu_runs.append(time.perf_counter() - c0)
+                else:
+                    scratch.fill_(r & 0xFF)
+                    a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    check(lib.gdn_prefill(*PF[0]), "gdn_prefill")
+                    b2.record(stream)
+                    torch.cuda.synchronize()
+                    gpu_alt.append(a.elapsed_time(b2) * 1e3)
+            r += 1
+        cpu_s = float(np.mean(cpu_runs))
         # one thread on a bounded sample: 2 of the 32 value heads, scaled to the workload
         c1 = time.perf_counter()
         orc.seq(qa, ka, va, ga, ba, pairs=[(0, 0), (0, 1)], nthreads=1, rows_per_item=8)
@@ -546,12 +563,15 @@ def main():
             pass
         o_gpu = sets[0]["o"].float().cpu().numpy()
         s_gpu = sets[0]["state_out"].cpu().numpy()
-        err = lambda x, r: float(np.max(np.abs(x - r)) / np.max(np.abs(r)))  # noqa: E731
+        err = lambda x, r_: float(np.max(np.abs(x - r_)) / np.max(np.abs(r_)))  # noqa: E731
         out["cpu_baseline"] = {"value": round(T / cpu_s, 1), "unit": "tokens/s", "cores": threads,
                                "kind": "oracle",
                                "sample": f"the full prefill workload (T={T}, all {Hv} value heads), "
-                                         f"fp64 token-by-token scan, {threads} threads, run "
-                                         f"{reps} times in {cpu_total:.1f} s ({cpu_s:.3f} s each)",
+                                         f"fp64 token-by-token scan on {threads} threads, "
+                                         f"{len(cpu_runs)} runs ({sum(cpu_runs):.1f} s) alternated "
+                                         f"with {len(gpu_alt)} cold GPU prefill calls, the order "
+                                         f"of the two legs swapped every round",
+                               "gpu_us_alternated": round(float(np.mean(gpu_alt)), 2),
                                "single_thread_value": round(T / one_s, 1),
                                "single_thread_sample": f"value heads 0 and 1 of the same workload on "
                                                        f"1 thread, scaled by {Hv // 2}",

@@ -112,8 +112,7 @@ inline hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     constexpr int RPB = (2 * RIT < DV) ? 2 * RIT : DV;
     constexpr int NBLK = DV / RPB;
     dim3 grid((unsigned)(p.B * p.Hv * NBLK));
-    decode_kernel<E, DK, DV><<<grid, 256, 0, stream>>>(p);
-    return hipGetLastError();
+    return launch_kernel(decode_kernel<E, DK, DV>, grid, dim3(256), stream, p);
 }
 
 }  // namespace gdn

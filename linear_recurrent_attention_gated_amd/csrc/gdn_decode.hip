@@ -21,8 +21,7 @@ hipError_t copy_state(const float* in, float* out, size_t n, hipStream_t s) {
     if (n == 0 || in == out) return hipSuccess;
     size_t blocks = (n + 255) / 256;
     if (blocks > 4096) blocks = 4096;
-    copy_state_kernel<<<dim3((unsigned)blocks), 256, 0, s>>>(in, out, n);
-    return hipGetLastError();
+    return launch_kernel(copy_state_kernel, dim3((unsigned)blocks), dim3(256), s, in, out, n);
 }
 
 }  // namespace gdn

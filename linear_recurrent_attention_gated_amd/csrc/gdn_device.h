@@ -205,6 +205,17 @@ __device__ __forceinline__ void group_sum3(float& x, float& y, float& z) {
     }
 }
 
+// Launches kernel<<<grid, block, 0, s>>>(args...) and returns the status of that launch
+// alone.  hipLaunchKernel reports its own failure directly, so an error left pending by
+// earlier, unrelated HIP work on the calling thread is neither consumed nor reported as this
+// launch's.
+template <typename... A>
+inline hipError_t launch_kernel(void (*kernel)(A...), dim3 grid, dim3 block, hipStream_t s,
+                                A... args) {
+    void* argv[sizeof...(A) > 0 ? sizeof...(A) : 1] = {static_cast<void*>(&args)...};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, s);
+}
+
 // Workgroup barrier for LDS traffic: wait until this wave's LDS reads and writes have
 // completed, then synchronise the waves.  Unlike __syncthreads() it does not wait for
 // outstanding global loads or stores, so prefetches and output stores stay in flight across

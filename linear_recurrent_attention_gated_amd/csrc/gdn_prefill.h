@@ -1039,7 +1039,8 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
                 for (int j = 0; j < 4; ++j) os[(rq + j) * LDO + rl] = X::from_f(acc[j]);
                 wave_lds_sync();
                 constexpr int PPR = (int)sizeof(E);
-                const int tok = lane / PPR, piece = lane % PPR;
+                // lanes past the tile's 16 rows (bf16: lanes 32..63) read row tok & 15 and store nothing
+                const int tok = (lane / PPR) & 15, piece = lane % PPR;
                 const uint4 v = *reinterpret_cast<const uint4*>(os + tok * LDO + piece * EPV);
                 const int t = t0 + m * 16 + tok;
                 if (lane < 16 * PPR && (!TAIL || t < T))
@@ -1100,17 +1101,16 @@ inline hipError_t launch_prefill(const PrefillParams& p, int stages, hipStream_t
             constexpr bool NORM = decltype(norm)::value;
             const int cap = intra_capacity<E, DK, DV, C, NORM>();
             const int grid = std::min(nitems, std::max(unit, cap / unit * unit));
-            intra_chunk_kernel<E, DK, DV, C, NORM><<<grid, kThreads, 0, stream>>>(p);
+            return launch_kernel(intra_chunk_kernel<E, DK, DV, C, NORM>, dim3(grid), dim3(kThreads),
+                                 stream, p);
         };
-        if (p.qk_norm) go(std::true_type{});
-        else go(std::false_type{});
-        hipError_t e = hipGetLastError();
+        const hipError_t e = p.qk_norm ? go(std::true_type{}) : go(std::false_type{});
         if (e != hipSuccess) return e;
     }
     if (stages & 2) {
-        dim3 g2(p.B * p.Hv * (DV / 16));
-        inter_chunk_kernel<E, DK, DV, C, sizeof(E) == 2><<<g2, kScanThreads, 0, stream>>>(p);
-        return hipGetLastError();
+        const dim3 g2(p.B * p.Hv * (DV / 16));
+        return launch_kernel(inter_chunk_kernel<E, DK, DV, C, sizeof(E) == 2>, g2, dim3(kScanThreads),
+                             stream, p);
     }
     return hipSuccess;
 }

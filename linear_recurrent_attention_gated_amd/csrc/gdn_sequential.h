@@ -198,9 +198,8 @@ template <typename E, int DK, int DV>
 inline hipError_t launch_sequential(const PrefillParams& p, hipStream_t stream) {
     using S = SeqShape<DK, DV>;
     const dim3 grid((unsigned)(p.B * p.Hv * S::NBLK));
-    if (p.qk_norm) sequential_kernel<E, DK, DV, true><<<grid, S::NTH, 0, stream>>>(p);
-    else sequential_kernel<E, DK, DV, false><<<grid, S::NTH, 0, stream>>>(p);
-    return hipGetLastError();
+    if (p.qk_norm) return launch_kernel(sequential_kernel<E, DK, DV, true>, grid, dim3(S::NTH), stream, p);
+    return launch_kernel(sequential_kernel<E, DK, DV, false>, grid, dim3(S::NTH), stream, p);
 }
 
 }  // namespace gdn

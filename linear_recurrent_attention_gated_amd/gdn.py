@@ -6,6 +6,7 @@ entry points of the same names, and a nonzero status raises ``GdnError``.  Every
 step of the computation runs in the library's HIP kernels; there is no fallback.
 PyTorch provides device memory and streams.
 """
+import contextlib
 import ctypes
 import os
 
@@ -207,6 +208,18 @@ def _decode_call(fn, q, k, v, g, beta, state_in, state_out, o, stream):
 
 # -- conveniences that allocate outputs with torch --------------------------------------------
 
+def _alloc_ctx(stream):
+    """Allocation context of the stream the kernels are enqueued on.  torch's caching allocator
+    ties a block to the stream it was allocated on: a workspace freed on return is then reused
+    only by later work on that same stream (ordered after our kernels), never by another
+    stream while our kernels may still read it."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream))
+    return torch.cuda.stream(stream)
+
+
 def prefill(q, k, v, g, beta, state=None, chunk=64, workspace=None, stream=None, qk_norm=False,
             path="blockwise"):
     """Returns (o, state_out); allocates o, state_out and (if needed and not given) the
@@ -214,14 +227,15 @@ def prefill(q, k, v, g, beta, state=None, chunk=64, workspace=None, stream=None,
     (gdn_prefill / gdn_prefill_qknorm), "sequential" or "auto" (gdn_prefill_ex)."""
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
-    o = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=q.device)
-    s_out = torch.empty((B, Hv, dv, dk), dtype=torch.float32, device=q.device)
     flags = PATHS[path] | (GDN_QK_NORM if qk_norm else 0)
     seq = path == "sequential" or (
         path == "auto" and T <= gdn_prefill_sequential_max_tokens(B, Hk, Hv, dk, dv, q.dtype))
-    if workspace is None and T > 0 and not seq:
-        nb = gdn_prefill_workspace_bytes(B, T, Hk, Hv, dk, dv, chunk, q.dtype)
-        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    with _alloc_ctx(stream):
+        o = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=q.device)
+        s_out = torch.empty((B, Hv, dv, dk), dtype=torch.float32, device=q.device)
+        if workspace is None and T > 0 and not seq:
+            nb = gdn_prefill_workspace_bytes(B, T, Hk, Hv, dk, dv, chunk, q.dtype)
+            workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
     if path == "blockwise":
         (gdn_prefill_qknorm if qk_norm else gdn_prefill)(q, k, v, g, beta, state, o, s_out, chunk,
                                                          workspace, stream)
@@ -233,7 +247,8 @@ def prefill(q, k, v, g, beta, state=None, chunk=64, workspace=None, stream=None,
 def decode_step(q, k, v, g, beta, state, stream=None, qk_norm=False):
     """Updates ``state`` in place and returns o [B,Hv,dv].  qk_norm: L2-normalise q and k
     inside the kernel (gdn_decode_step_qknorm)."""
-    o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+    with _alloc_ctx(stream):
+        o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
     (gdn_decode_step_qknorm if qk_norm else gdn_decode_step)(q, k, v, g, beta, state, state, o,
                                                              stream)
     return o

@@ -13,10 +13,18 @@ TOL_O = 2e-2
 TOL_S = 1e-2
 
 
+# Parity figures of the run, printed by tests/conftest.py in pytest's terminal summary (so
+# they show for passing tests and under -q as well).
+REPORT = []
+
+
 def say(*a):
-    """Name the case before a GPU step (flushed, so it survives a crashed run)."""
+    """Name the case before a GPU step (flushed, so it survives a crashed run).  Lines that
+    carry error figures also go to the end-of-run parity summary."""
     print("[gpu-case]", *a, flush=True)
     sys.stdout.flush()
+    if any("error" in str(x) for x in a):
+        REPORT.append(" ".join(f"{x:.3e}" if isinstance(x, float) else str(x) for x in a))
 
 
 def nrel(x, ref):

@@ -71,7 +71,7 @@ def test_prefill_matches_oracle(case, dt):
     o, s = run_prefill(d, chunk, d["state"])
     o_ref, s_ref = oracle_prefill(d, d["state"])
     eo, es = nrel(o, o_ref), nrel(s, s_ref)
-    say("errors", eo, es)
+    say("prefill errors", dt, case, eo, es)
     assert eo < TOL_O and es < TOL_S
     if dt == "f32":
         assert eo < 1e-4 and es < 1e-4
@@ -135,7 +135,7 @@ def test_decode_matches_oracle(dims, dt):
     torch.cuda.synchronize()
     o_ref, s_ref = oracle_prefill(d, d["state"])
     eo, es = nrel(np32(o), o_ref[:, 0]), nrel(st.cpu().numpy(), s_ref)
-    say("decode errors", eo, es)
+    say("decode errors", dt, dims, eo, es)
     assert eo < TOL_O and es < TOL_S
     # fp32 VALU on exact inputs: rounding only (plus the bf16 rounding of o itself)
     assert es < 1e-6 and eo < (1e-5 if dt == "f32" else 8e-3)

@@ -41,7 +41,7 @@ def test_prefill_qknorm_matches_oracle(case, dt):
     torch.cuda.synchronize()
     o_ref, s_ref = oracle_prefill(d, d["state"], qk_norm=True)
     eo, es = nrel(np32(o), o_ref), nrel(s.cpu().numpy(), s_ref)
-    say("errors", eo, es)
+    say("prefill qknorm errors", dt, case, eo, es)
     assert eo < TOL_O and es < TOL_S
     if dt == "f32":
         assert eo < 1e-4 and es < 1e-4
@@ -112,6 +112,6 @@ def test_decode_qknorm_matches_oracle(dims, dt):
     torch.cuda.synchronize()
     o_ref, s_ref = oracle_prefill(d, d["state"], qk_norm=True)
     eo, es = nrel(np32(o), o_ref[:, 0]), nrel(st.cpu().numpy(), s_ref)
-    say("decode qknorm errors", eo, es)
+    say("decode qknorm errors", dt, dims, eo, es)
     assert eo < TOL_O and es < TOL_S
     assert es < 1e-6 and eo < (1e-5 if dt == "f32" else 8e-3)

@@ -45,7 +45,7 @@ def test_sequential_matches_oracle(case, qk_norm, dt):
     torch.cuda.synchronize()
     o_ref, s_ref = oracle_prefill(d, d["state"], qk_norm=qk_norm)
     eo, es = nrel(np32(o), o_ref), nrel(s.cpu().numpy(), s_ref)
-    say("errors", eo, es)
+    say("sequential errors", dt, qk_norm, case, eo, es)
     assert eo < TOL_O and es < TOL_S
     # fp32 arithmetic on exact inputs: only the output's own rounding is visible in bf16
     assert es < 1e-4 and eo < (1e-4 if dt == "f32" else 8e-3)

@@ -1,11 +1,10 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark
 times, plus the properties the pages state or the method implies.
 
-Full sizes: the 4096-token prefill (all heads against the oracle, bf16 and fp32),
-the 32768-token continuation from a nonzero state (sampled heads -- every head is
-an independent recurrence, so the oracle computes the sampled ones exactly), the
-131072-token long-memory prefill (sampled heads) and its prefix sweep, and one
-decode token through 30 layers (looped and batched).
+Full sizes, each in the bf16 build (bf16 q/k/v/o, fp32 gates and state) and in the
+all-fp32 build, every value head against the oracle: the 4096-token prefill, the
+32768-token continuation from a nonzero state, the 131072-token long-memory prefill
+and its prefix sweep, and one decode token through 30 layers (looped and batched).
 
 Properties: segmenting a prompt and carrying the state gives the same output
 ("Optimizing on-device inference for Apple Silicon", section "Bound temporary
@@ -27,9 +26,6 @@ from tests.gpu_util import TOL_O, TOL_S, nrel, np32, oracle_prefill, say, to_dev
 pytestmark = pytest.mark.gpu
 
 NTHREADS = 16
-# value heads sampled for the long workloads: both heads of one key head, and heads spread
-# over the other key heads
-SAMPLED = [0, 1, 13, 22, 31]
 
 
 def gpu_prefill(d, chunk, state=None, dtype_ws=None):
@@ -40,21 +36,32 @@ def gpu_prefill(d, chunk, state=None, dtype_ws=None):
     return o, s
 
 
-@pytest.fixture(scope="module")
-def c2_bf16():
-    d = workload_inputs(PREFILL_4K, torch.bfloat16)
+DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def per_head_errors(o_g, s_g, o_ref, s_ref, heads):
+    """Normwise errors of every value head (each head is an independent recurrence, so each
+    is held to the tolerance on its own); returns the worst pair."""
+    worst_o = worst_s = 0.0
+    for i, h in enumerate(heads):
+        eo, es = nrel(o_g[0, :, h], o_ref[0, :, i]), nrel(s_g[0, h], s_ref[0, i])
+        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+        assert eo < TOL_O and es < TOL_S, (h, eo, es)
+    return worst_o, worst_s
+
+
+@pytest.fixture(scope="module", params=sorted(DTYPES))
+def c2(request):
+    """The 4096-token prefill workload and its oracle result, in either build."""
+    dt = request.param
+    d = workload_inputs(PREFILL_4K, DTYPES[dt])
     o_ref, s_ref = oracle_prefill(d, nthreads=NTHREADS)
-    return d, o_ref, s_ref
+    return dt, d, o_ref, s_ref
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
-def test_prefill_4k_all_heads(dt, c2_bf16):
+def test_prefill_4k_all_heads(c2):
     w = PREFILL_4K
-    if dt == "bf16":
-        d, o_ref, s_ref = c2_bf16
-    else:
-        d = workload_inputs(w, torch.float32)
-        o_ref, s_ref = oracle_prefill(d, nthreads=NTHREADS)
+    dt, d, o_ref, s_ref = c2
     say("prefill 4k", dt)
     o, s = gpu_prefill(d, w.chunk)
     eo, es = nrel(np32(o), o_ref), nrel(s.cpu().numpy(), s_ref)
@@ -62,66 +69,72 @@ def test_prefill_4k_all_heads(dt, c2_bf16):
     assert eo < TOL_O and es < TOL_S
 
 
-def test_continuation_32k_from_nonzero_state(c2_bf16):
+def test_continuation_32k_from_nonzero_state(c2):
+    # every value head of the 32768-token continuation against the oracle, from the oracle's
+    # final state of the 4096-token prefill (same build), then the GPU's own chained result
     w = CONTINUATION_32K
-    d0, _, s_c2 = c2_bf16
-    start = s_c2.astype(np.float32)          # the oracle's final state of the 4096-token prefill
-    d = workload_inputs(w, torch.bfloat16)
-    pairs = [(0, h) for h in SAMPLED]
-    say("continuation 32k")
+    dt, d0, _, s_c2 = c2
+    start = s_c2.astype(np.float32)
+    d = workload_inputs(w, DTYPES[dt])
+    say("continuation 32k", dt)
     o, s = gpu_prefill(d, w.chunk, start)
-    o_ref, s_ref = oracle_prefill(d, start.astype(np.float64), pairs=pairs, nthreads=NTHREADS)
+    o_ref, s_ref = oracle_prefill(d, start.astype(np.float64), nthreads=NTHREADS)
     o_g, s_g = np32(o), s.cpu().numpy()
-    for i, h in enumerate(SAMPLED):
-        eo, es = nrel(o_g[0, :, h], o_ref[i]), nrel(s_g[0, h], s_ref[i])
-        say("continuation head", h, eo, es)
-        assert eo < TOL_O and es < TOL_S
+    heads = list(range(w.Hv))
+    o_ref = o_ref.reshape(1, w.T, w.Hv, w.dv)
+    eo, es = per_head_errors(o_g, s_g, o_ref, s_ref, heads)
+    say("continuation 32k worst head errors", dt, eo, es)
     # chained on the GPU: its own 4096-token state carried into the continuation
     _, s_gpu_c2 = gpu_prefill(d0, PREFILL_4K.chunk)
     o2, s2 = gpu_prefill(d, w.chunk, s_gpu_c2.cpu().numpy())
-    o2g, s2g = np32(o2), s2.cpu().numpy()
-    for i, h in enumerate(SAMPLED):
-        assert nrel(o2g[0, :, h], o_ref[i]) < TOL_O and nrel(s2g[0, h], s_ref[i]) < TOL_S
+    eo2, es2 = per_head_errors(np32(o2), s2.cpu().numpy(), o_ref, s_ref, heads)
+    say("continuation 32k chained worst head errors", dt, eo2, es2)
 
 
-@pytest.fixture(scope="module")
-def c4():
-    d = workload_inputs(LONG_128K, torch.bfloat16)
-    say("long 128k: GPU run")
+@pytest.fixture(scope="module", params=sorted(DTYPES))
+def c4(request):
+    dt = request.param
+    d = workload_inputs(LONG_128K, DTYPES[dt])
+    say("long 128k: GPU run", dt)
     o, s = gpu_prefill(d, LONG_128K.chunk)
-    return d, np32(o), s.cpu().numpy()
+    return dt, d, np32(o), s.cpu().numpy()
 
 
-def test_long_128k_sampled_heads(c4):
-    d, o_g, s_g = c4
-    pairs = [(0, h) for h in SAMPLED[:3]]
-    o_ref, s_ref = oracle_prefill(d, pairs=pairs, nthreads=NTHREADS)
-    for i, (_, h) in enumerate(pairs):
-        eo, es = nrel(o_g[0, :, h], o_ref[i]), nrel(s_g[0, h], s_ref[i])
-        say("long head", h, eo, es)
-        assert eo < TOL_O and es < TOL_S
-        assert np.all(np.isfinite(o_g[0, :, h]))
+def test_long_128k_all_heads(c4):
+    # the fixed-size state carries 131072 tokens of long-memory gates (a near 1): the longest
+    # accumulation of rounding in the fp32 state of either build, checked on every value head
+    dt, d, o_g, s_g = c4
+    w = LONG_128K
+    say("long 128k oracle", dt)
+    o_ref, s_ref = oracle_prefill(d, nthreads=NTHREADS)
+    assert np.all(np.isfinite(o_g)) and np.all(np.isfinite(s_g))
+    eo, es = per_head_errors(o_g, s_g, o_ref.reshape(1, w.T, w.Hv, w.dv), s_ref, list(range(w.Hv)))
+    say("long 128k worst head errors", dt, eo, es)
 
 
 def test_long_sweep_prefixes(c4):
     # the sweep T = 256, 512, ..., 65536 runs prefixes of the same draw; chunk-aligned prefixes
     # go through identical chunk computations, so their outputs equal the full run's bitwise
-    d, o_full, _ = c4
+    dt, d, o_full, _ = c4
     for T in [256 << i for i in range(9)]:
         dp = {k: (None if v is None else v[:, :T].contiguous()) for k, v in d.items()}
-        say("sweep prefix", T)
+        say("sweep prefix", dt, T)
         o, _ = gpu_prefill(dp, LONG_128K.chunk)
         assert np.array_equal(np32(o), o_full[:, :T]), T
 
 
-def test_decode_30_layers_looped_and_batched():
-    layers = [decode_inputs(l) for l in range(DECODE_LAYERS)]
+@pytest.mark.parametrize("dt", sorted(DTYPES))
+def test_decode_30_layers_looped_and_batched(dt):
+    # one token through 30 independent layers at 16 key / 32 value heads, d = 128: 30 B = 1
+    # launches and one B = 30 launch give the same bits, and every layer meets the tolerance
+    dtype = DTYPES[dt]
+    layers = [decode_inputs(l, dtype) for l in range(DECODE_LAYERS)]
     cat = {k: torch.cat([L[k] for L in layers]).cuda() for k in layers[0]}
     st_loop = cat["state"].clone()
     st_b = cat["state"].clone()
-    o_loop = torch.empty((DECODE_LAYERS, 32, 128), dtype=torch.bfloat16, device="cuda")
+    o_loop = torch.empty((DECODE_LAYERS, 32, 128), dtype=dtype, device="cuda")
     o_b = torch.empty_like(o_loop)
-    say("decode 30 layers")
+    say("decode 30 layers", dt)
     for l in range(DECODE_LAYERS):
         sl = slice(l, l + 1)
         gdn.gdn_decode_step(cat["q"][sl], cat["k"][sl], cat["v"][sl], cat["g"][sl],
@@ -134,9 +147,12 @@ def test_decode_30_layers_looped_and_batched():
     o_ref, s_ref = orc.decode_step(f(cat["q"].cpu()), f(cat["k"].cpu()), f(cat["v"].cpu()),
                                    f(cat["g"].cpu()), f(cat["beta"].cpu()),
                                    cat["state"].cpu().numpy().astype(np.float64))
+    worst_o = worst_s = 0.0
     for l in range(DECODE_LAYERS):
-        assert nrel(np32(o_loop[l]), o_ref[l]) < TOL_O
-        assert nrel(st_loop[l].cpu().numpy(), s_ref[l]) < 1e-6
+        eo, es = nrel(np32(o_loop[l]), o_ref[l]), nrel(st_loop[l].cpu().numpy(), s_ref[l])
+        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+        assert eo < TOL_O and es < 1e-6, (l, eo, es)
+    say("decode 30 layers worst layer errors", dt, worst_o, worst_s)
 
 
 def test_split_invariance_state_carry():
@@ -265,11 +281,11 @@ def test_prepare_then_scan_equals_one_call(dt):
 
 
 def test_long_128k_bounded_workspace(c4):
-    # the 131072-token prompt with a 256 MiB workspace (the one-pass workspace is ~3 GiB)
-    d, o_full, s_full = c4
+    # the 131072-token prompt with a 256 MiB workspace (the one-pass workspace is 2.5-5 GiB)
+    dt, d, o_full, s_full = c4
     w = LONG_128K
-    full = gdn.gdn_prefill_workspace_bytes(w.B, w.T, w.Hk, w.Hv, w.dk, w.dv, w.chunk, torch.bfloat16)
+    full = gdn.gdn_prefill_workspace_bytes(w.B, w.T, w.Hk, w.Hv, w.dk, w.dv, w.chunk, DTYPES[dt])
     assert full > 8 * (256 << 20)
-    say("long 128k, bounded workspace")
+    say("long 128k, bounded workspace", dt)
     o, s = _prefill_with_workspace(d, w.chunk, 256 << 20)
     assert np.array_equal(np32(o), o_full) and np.array_equal(s.cpu().numpy(), s_full)
