@@ -37,9 +37,10 @@
  *     before anything is enqueued.  Asynchronous kernel faults surface on the stream.
  *   - Shapes supported: dk, dv in {32, 64, 128}; Hk >= 1; Hv a multiple of Hk; B >= 1;
  *     chunk in {16, 32, 64}; any T >= 0 (a final chunk shorter than `chunk` is exact).
- *   - Thread safety: the only global state is a per-device cache of an occupancy query,
- *     filled idempotently on first use; concurrent calls on different streams with
- *     disjoint buffers are safe.
+ *   - Thread safety: the only global state is a per-device cache of an occupancy query and
+ *     of the scratch array's address (gdn_prefill_noalloc), each filled idempotently on first
+ *     use; concurrent calls on different streams with disjoint buffers are safe, except
+ *     overlapping gdn_prefill_noalloc calls on one GPU (see there).
  *   - Return value: a gdn_status; GDN_OK (0) on success.
  */
 #ifndef GDN_H_
@@ -167,6 +168,29 @@ gdn_status gdn_prefill_scan(const void *q, const void *k, const void *v, const f
                             int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                             gdn_dtype dtype, void *workspace, size_t workspace_bytes,
                             void *stream);
+
+/* Size of the device array gdn_prefill_noalloc uses as its workspace (one per GPU). */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* gdn_prefill for callers that cannot allocate device memory: code under HIP-graph capture,
+ * tight serving loops, and harnesses that forbid hipMalloc.  Arguments, results, aliasing
+ * rules and status codes are those of gdn_prefill, without the workspace: the blocks between
+ * the two kernels go to a device array of GDN_NOALLOC_SCRATCH_BYTES inside the library, one
+ * copy per GPU, held until the process ends.  Nothing is allocated or freed, by this call or
+ * by the library.  A prompt whose one-pass workspace (gdn_prefill_workspace_bytes) exceeds the
+ * array runs in segments of whole chunks, exactly as gdn_prefill with a smaller workspace, so
+ * the result equals gdn_prefill's bit for bit.  GDN_ERR_WORKSPACE when even one chunk's blocks
+ * do not fit (B * Hv too large at these head sizes); GDN_ERR_HIP if the array's device address
+ * cannot be obtained (taken once per device, on the first call with that device current).
+ * The array keeps the last call's contents, none of which a later call relies on (every
+ * value the second kernel reads is written by the first in the same call).  All calls on one
+ * GPU share the array: calls that overlap in time on that GPU (on different streams, or from
+ * different host threads onto different streams) race and must be serialised by the caller;
+ * calls in order on one stream are safe. */
+gdn_status gdn_prefill_noalloc(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const float *state_in, void *o,
+                               float *state_out, int B, int T, int Hk, int Hv, int dk, int dv,
+                               int chunk, gdn_dtype dtype, void *stream);
 
 /* One-token recurrent update (decode step), in place or out of place.
  *   q, k       [B, Hk, dk] dtype         v  [B, Hv, dv] dtype

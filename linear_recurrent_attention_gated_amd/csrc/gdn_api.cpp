@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/gdn.h"
 #include "gdn_launch.h"
 
@@ -75,13 +77,42 @@ size_t gdn_prefill_workspace_bytes(int B, int T, int Hk, int Hv, int dk, int dv,
 
 }  // extern "C"
 
+// ---- allocation-free prefill ------------------------------------------------------------
+// The workspace of gdn_prefill_noalloc: a file-scope device array, one copy per GPU, held until
+// the process ends.  In host code `scratch` only names the symbol; its device address comes
+// from hipGetSymbolAddress, once per device (with that device current), and only that address
+// is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`.
+gdn_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDN_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GDN_ERR_HIP;
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return GDN_OK;
+}
+
+}  // namespace
+
 namespace {
 
 gdn_status prefill_stages(const void* q, const void* k, const void* v, const float* g,
                           const float* beta, const float* state_in, void* o, float* state_out,
                           int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype dtype,
                           void* workspace, size_t workspace_bytes, void* stream, int stages,
-                          int qk_norm, bool sequential) {
+                          int qk_norm, bool sequential, bool noalloc = false) {
     const gdn_status sc = shape_check(B, T, Hk, Hv, dk, dv, chunk, dtype, true);
     if (sc != GDN_OK) return sc;
     if (!state_out) return GDN_ERR_NULL;
@@ -121,6 +152,13 @@ gdn_status prefill_stages(const void* q, const void* k, const void* v, const flo
         const hipError_t e = dtype == GDN_BF16 ? gdn::sequential_bf16(dk, dv, p, st)
                                                : gdn::sequential_f32(dk, dv, p, st);
         return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    }
+    if (noalloc) {   // every argument has been validated: now (only) look up the array
+        if (layout(B, chunk, Hk, Hv, dk, dv, chunk, dtype).total > GDN_NOALLOC_SCRATCH_BYTES)
+            return GDN_ERR_WORKSPACE;
+        const gdn_status st = scratch_address(&workspace);
+        if (st != GDN_OK) return st;
+        workspace_bytes = GDN_NOALLOC_SCRATCH_BYTES;
     }
     if (!workspace) return GDN_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
@@ -226,6 +264,14 @@ gdn_status gdn_prefill_scan(const void* q, const void* k, const void* v, const f
                             void* stream) {
     return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
                           dtype, workspace, workspace_bytes, stream, 2, 0, false);
+}
+
+gdn_status gdn_prefill_noalloc(const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, const float* state_in, void* o, float* state_out,
+                               int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                               gdn_dtype dtype, void* stream) {
+    return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
+                          dtype, nullptr, 0, stream, 3, 0, false, true);
 }
 
 }  // extern "C"

@@ -21,7 +21,9 @@ _STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUP
            4: "GDN_ERR_ALIGN", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP"}
 EXPORTS = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_qknorm", "gdn_prefill_ex",
            "gdn_prefill_sequential_max_tokens", "gdn_prefill_prepare", "gdn_prefill_scan",
-           "gdn_decode_step", "gdn_decode_step_qknorm", "gdn_status_string", "gdn_abi_version")
+           "gdn_decode_step", "gdn_decode_step_qknorm", "gdn_status_string", "gdn_abi_version",
+           "gdn_prefill_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES
 
 # flags of gdn_prefill_ex
 GDN_QK_NORM = 1
@@ -56,6 +58,8 @@ def lib():
         for fn in ("gdn_decode_step", "gdn_decode_step_qknorm"):
             getattr(L, fn).argtypes = [P] * 8 + [I] * 6 + [P]
             getattr(L, fn).restype = I
+        L.gdn_prefill_noalloc.argtypes = [P] * 8 + [I] * 8 + [P]
+        L.gdn_prefill_noalloc.restype = I
         L.gdn_prefill_ex.argtypes = [P] * 8 + [I] * 8 + [P, Z, P, ctypes.c_uint]
         L.gdn_prefill_ex.restype = I
         L.gdn_prefill_sequential_max_tokens.argtypes = [I] * 6
@@ -132,6 +136,24 @@ def gdn_prefill_ex(q, k, v, g, beta, state_in, o, state_out, chunk, workspace, f
     arguments as gdn_prefill, the workspace may be None on the sequential path."""
     _prefill_call("gdn_prefill_ex", q, k, v, g, beta, state_in, o, state_out, chunk, workspace,
                   stream, (int(flags),))
+
+
+def gdn_prefill_noalloc(q, k, v, g, beta, state_in, o, state_out, chunk, stream=None):
+    """Calls gdn_prefill_noalloc: gdn_prefill with the library's fixed device array as the
+    workspace (nothing allocated); arguments as gdn_prefill without the workspace."""
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dt = _dt(q)
+    for t in (k, v, o):
+        if _dt(t) != dt:
+            raise TypeError("q, k, v and o must share one dtype")
+    for t, nm in ((g, "g"), (beta, "beta"), (state_in, "state_in"), (state_out, "state_out")):
+        _f32(t, nm)
+    rc = lib().gdn_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+                                   _ptr(o), _ptr(state_out), B, T, Hk, Hv, dk, dv, int(chunk), dt,
+                                   _stream(stream))
+    if rc != 0:
+        raise GdnError("gdn_prefill_noalloc", rc)
 
 
 def gdn_prefill_sequential_max_tokens(B, Hk, Hv, dk, dv, dtype) -> int:

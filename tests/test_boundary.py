@@ -99,6 +99,24 @@ def test_prefill_rejects(kw, code, fn):
     assert _prefill(fn=fn, **kw) == code
 
 
+@pytest.mark.parametrize("kw,code", [c for c in PREFILL_ERRORS if not ({"ws", "ws_bytes"} & set(c[0]))]
+                         + [(dict(B=64, T=64, Hk=16, Hv=32, dk=128, dv=128, chunk=64), 6)])
+def test_prefill_noalloc_rejects(kw, code):
+    # gdn_prefill_noalloc validates every argument before it looks up its device array (the
+    # last case: one chunk's blocks, ~84 MB, exceed the 64 MiB array)
+    a = dict(q=BASE, k=BASE + 10 * MB, v=BASE + 20 * MB, g=BASE + 40 * MB, beta=BASE + 41 * MB,
+             state_in=BASE + 50 * MB, o=BASE + 60 * MB, state_out=BASE + 80 * MB, B=1, T=64, Hk=2,
+             Hv=4, dk=32, dv=32, chunk=16, dtype=0)
+    if "B" in kw:   # the large shape needs room between the fake buffers
+        a.update(k=BASE + 200 * MB, v=BASE + 400 * MB, g=BASE + 600 * MB, beta=BASE + 610 * MB,
+                 state_in=BASE + 700 * MB, o=BASE + 900 * MB, state_out=BASE + 1000 * MB)
+    a.update(kw)
+    rc = gdn.lib().gdn_prefill_noalloc(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state_in"],
+                                       a["o"], a["state_out"], a["B"], a["T"], a["Hk"], a["Hv"],
+                                       a["dk"], a["dv"], a["chunk"], a["dtype"], None)
+    assert rc == code
+
+
 @pytest.mark.parametrize("flags", [8, 2 | 4, 0x100])
 def test_prefill_ex_rejects_flags(flags):
     L = gdn.lib()
