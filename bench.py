@@ -111,7 +111,9 @@ def summarize_counters(fetch_dir, write_dir):
                            else ("intra_qknorm" if ", true>" in name else "intra") + ("" if el == "bf16" else "_f32")
                            if "intra_chunk_kernel" in name
                            else "decode_L%d" % (int(float(row.get("Grid_Size", "0"))) // (256 * 256))
-                           if "decode_kernel" in name else None)
+                           if "decode_kernel" in name
+                           else "decode_layers_L%d" % (int(float(row.get("Grid_Size", "0"))) // (256 * 256))
+                           if "decode_layers_kernel" in name else None)
                     if key is None:
                         continue
                     sums.setdefault(key, []).append(float(row["Counter_Value"]) * 1024.0)
@@ -267,6 +269,8 @@ def main():
         dd = {k: v.to(dev) for k, v in dec_cat.items()}
         dd["o"] = torch.empty((LAYERS, Hv, dv), dtype=torch.bfloat16, device=dev)
         s["dec"] = dd
+        # the same states again, each layer in an allocation of its own (not back to back)
+        s["dec_states"] = [dd["state"][l].clone() for l in range(LAYERS)]
         sets.append(s)
     torch.cuda.synchronize()
 
@@ -282,7 +286,18 @@ def main():
                 d["g"][l0].data_ptr(), d["beta"][l0].data_ptr(), st, st, d["o"][l0].data_ptr(),
                 nb, Hk, Hv, dk, dv, gdn.GDN_BF16, sh)
 
+    def layer_table(s):
+        d = s["dec"]
+        t = (gdn.DecodeLayer * LAYERS)()
+        for l in range(LAYERS):
+            st = s["dec_states"][l].data_ptr()
+            t[l] = gdn.DecodeLayer(d["q"][l].data_ptr(), d["k"][l].data_ptr(), d["v"][l].data_ptr(),
+                                   d["g"][l].data_ptr(), d["beta"][l].data_ptr(), st, st,
+                                   d["o"][l].data_ptr())
+        return t
+
     PF = [pf_args(s) for s in sets]
+    DEC_L = [layer_table(s) for s in sets]
     DEC = [[dec_args(s, l, 1) for l in range(LAYERS)] for s in sets]
     DEC_B = [dec_args(s, 0, LAYERS) for s in sets]
 
@@ -349,6 +364,20 @@ def main():
             evb[i - 3][1].record(stream)
     torch.cuda.synchronize()
     t_dec_b = np.array([a.elapsed_time(b) for a, b in evb]) * 1e3
+
+    # -- decode, one launch over a pointer table of the 30 separately allocated layers -----------
+    evl = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps + 3):
+        j = i % len(sets)
+        if i >= 3:
+            evl[i - 3][0].record(stream)
+        check(lib.gdn_decode_step_layers(DEC_L[j], LAYERS, 1, Hk, Hv, dk, dv, gdn.GDN_BF16, 0, sh),
+              "gdn_decode_step_layers")
+        if i >= 3:
+            evl[i - 3][1].record(stream)
+    torch.cuda.synchronize()
+    t_dec_l = np.array([a.elapsed_time(b) for a, b in evl]) * 1e3
 
     # -- decode as a HIP graph: the 30 sequential launches captured once per buffer set and
     # replayed (no host launch gaps between layers); cold like the main steps ----------------
@@ -457,6 +486,8 @@ def main():
     dec_gbs_b = dec_bytes_b / (dec_b_us * 1e-6) / 1e9
     dec_gbs_loop = dec_bytes_b / (float(t_dec.mean()) * 1e-6) / 1e9
     dec_g_us = float(t_dec_g.mean())
+    dec_l_us = float(t_dec_l.mean())
+    dec_gbs_l = dec_bytes_b / (dec_l_us * 1e-6) / 1e9
     dec_gbs_g = dec_bytes_b / (dec_g_us * 1e-6) / 1e9
 
     out = {
@@ -511,11 +542,19 @@ def main():
             "hbm_gbs_graph": round(dec_gbs_g, 1),
             "us_per_token_batched": round(dec_b_us, 2),
             "hbm_gbs_batched": round(dec_gbs_b, 1),
-            "roofline": {"kernel": "decode_kernel, one launch over the 30 layers (B=30)",
-                         "bound": "hbm", "achieved": round(dec_gbs_b, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(dec_gbs_b / HBM_PEAK_GBS, 4),
-                         "traffic": traffic_doc.get("decode_L%d_bytes" % LAYERS) if traffic_doc else None,
+            "us_per_token_layers": round(dec_l_us, 2),
+            "hbm_gbs_layers": round(dec_gbs_l, 1),
+            "roofline": {"kernel": "decode_layers_kernel, one launch over a pointer table of the 30 "
+                                   "separately allocated layers (gdn_decode_step_layers)",
+                         "bound": "hbm", "achieved": round(dec_gbs_l, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(dec_gbs_l / HBM_PEAK_GBS, 4),
+                         "traffic": traffic_doc.get("decode_layers_L%d_bytes" % LAYERS) if traffic_doc else None,
                          "algorithmic_bytes_per_launch": dec_bytes_b},
+            "roofline_batched": {"kernel": "decode_kernel, one launch over the 30 layers stored back "
+                                           "to back (B=30)",
+                                 "bound": "hbm", "achieved": round(dec_gbs_b, 1), "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "frac": round(dec_gbs_b / HBM_PEAK_GBS, 4),
+                                 "traffic": traffic_doc.get("decode_L%d_bytes" % LAYERS) if traffic_doc else None},
         },
     }
 

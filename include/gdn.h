@@ -212,6 +212,33 @@ gdn_status gdn_decode_step_qknorm(const void *q, const void *k, const void *v, c
                                   void *o, int B, int Hk, int Hv, int dk, int dv, gdn_dtype dtype,
                                   void *stream);
 
+/* One layer's tensors for gdn_decode_step_layers: exactly the arguments of gdn_decode_step.
+ *   q, k [B, Hk, dk] dtype; v, o [B, Hv, dv] dtype; g, beta [B, Hv] float;
+ *   state_in, state_out [B, Hv, dv, dk] float (state_out may equal state_in). */
+typedef struct {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const float *state_in;
+    float *state_out;
+    void *o;
+} gdn_decode_layer;
+
+/* One decode token through nlayers independent layers whose tensors live anywhere in memory
+ * ("Optimizing on-device inference for Apple Silicon", section "Overlap independent GPU work":
+ * independent work of a decode step is dispatched together rather than one dependent stage
+ * after another).  The same step as gdn_decode_step on every layer, with the same arguments
+ * per layer (layers[l], a HOST array read during the call), the sizes and dtype shared; the
+ * results are those of nlayers gdn_decode_step calls, bit for bit.  The pointer table travels
+ * in the kernel arguments: one launch per 32 layers, no device memory used or allocated, and
+ * the call may be captured in a HIP graph.  flags: 0 or GDN_QK_NORM (as
+ * gdn_decode_step_qknorm).  Besides gdn_decode_step's checks on each layer: GDN_ERR_NULL if
+ * layers is NULL, GDN_ERR_SHAPE if nlayers < 1, GDN_ERR_UNSUPPORTED for other flag bits, and
+ * GDN_ERR_ALIAS if an output of one layer overlaps any tensor of another (the layers run
+ * concurrently). */
+gdn_status gdn_decode_step_layers(const gdn_decode_layer *layers, int nlayers, int B, int Hk,
+                                  int Hv, int dk, int dv, gdn_dtype dtype, unsigned flags,
+                                  void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *gdn_status_string(gdn_status status);
 

@@ -278,25 +278,51 @@ gdn_status gdn_prefill_noalloc(const void* q, const void* k, const void* v, cons
 
 namespace {
 
+// The spans of one decode step's tensors: q, k, v, g, beta, state_in (inputs), state_out, o.
+struct DecodeSpans {
+    Span in[6], ss, so;
+};
+DecodeSpans decode_spans(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* state_in, float* state_out, void* o,
+                         int B, int Hk, int Hv, int dk, int dv, gdn_dtype dtype) {
+    const size_t es = elem_size(dtype);
+    DecodeSpans d;
+    d.in[0] = {q, (size_t)B * Hk * dk * es};
+    d.in[1] = {k, (size_t)B * Hk * dk * es};
+    d.in[2] = {v, (size_t)B * Hv * dv * es};
+    d.in[3] = {g, (size_t)B * Hv * 4};
+    d.in[4] = {beta, (size_t)B * Hv * 4};
+    d.in[5] = {state_in, (size_t)B * Hv * dv * dk * 4};
+    d.ss = {state_out, (size_t)B * Hv * dv * dk * 4};
+    d.so = {o, (size_t)B * Hv * dv * es};
+    return d;
+}
+
+// Pointer, alignment and overlap rules of one decode step (sizes already checked).
+gdn_status decode_check(const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const float* state_in, float* state_out, void* o, int B,
+                        int Hk, int Hv, int dk, int dv, gdn_dtype dtype) {
+    if (!q || !k || !v || !g || !beta || !state_in || !state_out || !o) return GDN_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(state_in, 16) || !aligned(state_out, 16) || !aligned(g, 4) || !aligned(beta, 4))
+        return GDN_ERR_ALIGN;
+    const DecodeSpans d = decode_spans(q, k, v, g, beta, state_in, state_out, o, B, Hk, Hv, dk, dv, dtype);
+    for (const Span& in : d.in)
+        if (overlap(d.so, in)) return GDN_ERR_ALIAS;
+    if (overlap(d.so, d.ss)) return GDN_ERR_ALIAS;
+    for (int i = 0; i < 5; ++i)
+        if (overlap(d.ss, d.in[i])) return GDN_ERR_ALIAS;
+    if (state_in != state_out && overlap(d.ss, d.in[5])) return GDN_ERR_ALIAS;
+    return GDN_OK;
+}
+
 gdn_status decode(const void* q, const void* k, const void* v, const float* g, const float* beta,
                   const float* state_in, float* state_out, void* o, int B, int Hk, int Hv, int dk,
                   int dv, gdn_dtype dtype, void* stream, int qk_norm) {
     const gdn_status sc = shape_check(B, 1, Hk, Hv, dk, dv, 16, dtype, false);
     if (sc != GDN_OK) return sc;
-    if (!q || !k || !v || !g || !beta || !state_in || !state_out || !o) return GDN_ERR_NULL;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-        !aligned(state_in, 16) || !aligned(state_out, 16) || !aligned(g, 4) || !aligned(beta, 4))
-        return GDN_ERR_ALIGN;
-    const size_t es = elem_size(dtype);
-    const Span sq{q, (size_t)B * Hk * dk * es}, sk{k, (size_t)B * Hk * dk * es},
-        sv{v, (size_t)B * Hv * dv * es}, sg{g, (size_t)B * Hv * 4}, sb{beta, (size_t)B * Hv * 4},
-        si{state_in, (size_t)B * Hv * dv * dk * 4}, ss{state_out, (size_t)B * Hv * dv * dk * 4},
-        so{o, (size_t)B * Hv * dv * es};
-    for (Span in : {sq, sk, sv, sg, sb, si, ss})
-        if (overlap(so, in)) return GDN_ERR_ALIAS;
-    for (Span in : {sq, sk, sv, sg, sb})
-        if (overlap(ss, in)) return GDN_ERR_ALIAS;
-    if (state_in != state_out && overlap(ss, si)) return GDN_ERR_ALIAS;
+    const gdn_status pc = decode_check(q, k, v, g, beta, state_in, state_out, o, B, Hk, Hv, dk, dv, dtype);
+    if (pc != GDN_OK) return pc;
 
     gdn::DecodeParams p;
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.state_in = state_in;
@@ -321,6 +347,54 @@ gdn_status gdn_decode_step_qknorm(const void* q, const void* k, const void* v, c
                                   void* o, int B, int Hk, int Hv, int dk, int dv, gdn_dtype dtype,
                                   void* stream) {
     return decode(q, k, v, g, beta, state_in, state_out, o, B, Hk, Hv, dk, dv, dtype, stream, 1);
+}
+
+gdn_status gdn_decode_step_layers(const gdn_decode_layer* layers, int nlayers, int B, int Hk,
+                                  int Hv, int dk, int dv, gdn_dtype dtype, unsigned flags,
+                                  void* stream) {
+    if (!layers) return GDN_ERR_NULL;
+    if (nlayers < 1) return GDN_ERR_SHAPE;
+    if (flags & ~(unsigned)GDN_QK_NORM) return GDN_ERR_UNSUPPORTED;
+    const gdn_status sc = shape_check(B, 1, Hk, Hv, dk, dv, 16, dtype, false);
+    if (sc != GDN_OK) return sc;
+    if ((int64_t)nlayers * B * Hv * (dv / 16) > INT32_MAX / 2) return GDN_ERR_SHAPE;
+    for (int l = 0; l < nlayers; ++l) {
+        const gdn_decode_layer& L = layers[l];
+        const gdn_status pc = decode_check(L.q, L.k, L.v, L.g, L.beta, L.state_in, L.state_out,
+                                           L.o, B, Hk, Hv, dk, dv, dtype);
+        if (pc != GDN_OK) return pc;
+    }
+    // the layers run concurrently: no output of one layer may overlap any tensor of another
+    for (int l = 0; l < nlayers; ++l) {
+        const gdn_decode_layer& L = layers[l];
+        const DecodeSpans a = decode_spans(L.q, L.k, L.v, L.g, L.beta, L.state_in, L.state_out, L.o,
+                                           B, Hk, Hv, dk, dv, dtype);
+        for (int m = 0; m < nlayers; ++m) {
+            if (m == l) continue;
+            const gdn_decode_layer& M = layers[m];
+            const DecodeSpans b = decode_spans(M.q, M.k, M.v, M.g, M.beta, M.state_in, M.state_out,
+                                               M.o, B, Hk, Hv, dk, dv, dtype);
+            for (const Span& out : {a.ss, a.so}) {
+                for (const Span& in : b.in)
+                    if (overlap(out, in)) return GDN_ERR_ALIAS;
+                if (overlap(out, b.ss) || overlap(out, b.so)) return GDN_ERR_ALIAS;
+            }
+        }
+    }
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    for (int l0 = 0; l0 < nlayers; l0 += gdn::kDecodeLayersPerLaunch) {
+        gdn::DecodeTable t;
+        t.nlayers = nlayers - l0 < gdn::kDecodeLayersPerLaunch ? nlayers - l0 : gdn::kDecodeLayersPerLaunch;
+        t.B = B; t.Hk = Hk; t.Hv = Hv; t.qk_norm = (flags & GDN_QK_NORM) ? 1 : 0;
+        for (int i = 0; i < gdn::kDecodeLayersPerLaunch; ++i) {
+            const gdn_decode_layer& L = layers[l0 + (i < t.nlayers ? i : 0)];
+            t.layer[i] = {L.q, L.k, L.v, L.g, L.beta, L.state_in, L.state_out, L.o};
+        }
+        const hipError_t e = dtype == GDN_BF16 ? gdn::decode_layers_bf16(dk, dv, t, st)
+                                               : gdn::decode_layers_f32(dk, dv, t, st);
+        if (e != hipSuccess) return GDN_ERR_HIP;
+    }
+    return GDN_OK;
 }
 
 const char* gdn_status_string(gdn_status s) {

@@ -38,8 +38,29 @@ struct DecodeParams {
     int qk_norm;          // nonzero: q and k are L2-normalised per head first
 };
 
+// Per-layer pointers of a launch over several independent layers (one decode token through
+// a layer stack); the sizes and flags are shared.  Passed by value as a kernel argument, so a
+// launch needs no device memory for it.
+constexpr int kDecodeLayersPerLaunch = 32;
+struct DecodeLayerPtrs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const float* state_in;
+    float* state_out;
+    void* o;
+};
+struct DecodeTable {
+    DecodeLayerPtrs layer[kDecodeLayersPerLaunch];
+    int nlayers, B, Hk, Hv;
+    int qk_norm;
+};
+
+// One workgroup's share of a decode step: block `wg` of the B * Hv * NBLK blocks of p.
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+__device__ __forceinline__ void decode_block(const DecodeParams& p, int wg) {
     using X = Elem<E>;
     constexpr int LPR = DK / 4;
     constexpr int RIT = 256 / LPR;
@@ -48,8 +69,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     constexpr int NBLK = DV / RPB;
     static_assert(RIT <= DV && NIT * RIT == RPB && NBLK * RPB == DV, "decode tiling");
 
-    const int blk = blockIdx.x % NBLK;
-    const int bh = blockIdx.x / NBLK;
+    const int blk = wg % NBLK;
+    const int bh = wg / NBLK;
     const int h = bh % p.Hv, b = bh / p.Hv;
     const int hk = h / (p.Hv / p.Hk);
     const int tid = threadIdx.x;
@@ -103,6 +124,37 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         st_stream4(p.state_out + row * DK + c0, ns);
         if (sub == 0) op[row] = X::from_f(a * sq + delta * kq);
     }
+}
+
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+    decode_block<E, DK, DV>(p, blockIdx.x);
+}
+
+// The same step over t.nlayers layers in one launch: workgroup w takes block w % per of layer
+// w / per (per = B * Hv * NBLK), so every layer's state is read and written exactly as by its
+// own decode_kernel launch.
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(256) void decode_layers_kernel(DecodeTable t) {
+    constexpr int NBLK = DV / ((2 * (256 / (DK / 4)) < DV) ? 2 * (256 / (DK / 4)) : DV);
+    const int per = t.B * t.Hv * NBLK;
+    const int l = blockIdx.x / per;
+    const DecodeLayerPtrs& lp = t.layer[l];
+    DecodeParams p;
+    p.q = lp.q; p.k = lp.k; p.v = lp.v; p.g = lp.g; p.beta = lp.beta;
+    p.state_in = lp.state_in; p.state_out = lp.state_out; p.o = lp.o;
+    p.B = t.B; p.Hk = t.Hk; p.Hv = t.Hv; p.qk_norm = t.qk_norm;
+    decode_block<E, DK, DV>(p, blockIdx.x - l * per);
+}
+
+template <typename E, int DK, int DV>
+inline hipError_t launch_decode_layers(const DecodeTable& t, hipStream_t stream) {
+    constexpr int LPR = DK / 4;
+    constexpr int RIT = 256 / LPR;
+    constexpr int RPB = (2 * RIT < DV) ? 2 * RIT : DV;
+    constexpr int NBLK = DV / RPB;
+    const dim3 grid((unsigned)(t.nlayers * t.B * t.Hv * NBLK));
+    return launch_kernel(decode_layers_kernel<E, DK, DV>, grid, dim3(256), stream, t);
 }
 
 template <typename E, int DK, int DV>

@@ -26,6 +26,10 @@ hipError_t sequential_f32(int dk, int dv, const PrefillParams& p, hipStream_t s)
 hipError_t decode_bf16(int dk, int dv, const DecodeParams& p, hipStream_t s);
 hipError_t decode_f32(int dk, int dv, const DecodeParams& p, hipStream_t s);
 
+// One launch over up to kDecodeLayersPerLaunch layers (gdn_decode.h).
+hipError_t decode_layers_bf16(int dk, int dv, const DecodeTable& t, hipStream_t s);
+hipError_t decode_layers_f32(int dk, int dv, const DecodeTable& t, hipStream_t s);
+
 // T == 0: state_out <- state_in (or zeros).
 hipError_t copy_state(const float* in, float* out, size_t n, hipStream_t s);
 

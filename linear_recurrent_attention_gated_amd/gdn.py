@@ -22,7 +22,7 @@ _STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUP
 EXPORTS = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_qknorm", "gdn_prefill_ex",
            "gdn_prefill_sequential_max_tokens", "gdn_prefill_prepare", "gdn_prefill_scan",
            "gdn_decode_step", "gdn_decode_step_qknorm", "gdn_status_string", "gdn_abi_version",
-           "gdn_prefill_noalloc")
+           "gdn_prefill_noalloc", "gdn_decode_step_layers")
 NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES
 
 # flags of gdn_prefill_ex
@@ -30,6 +30,12 @@ GDN_QK_NORM = 1
 GDN_PATH_SEQUENTIAL = 2
 GDN_PATH_AUTO = 4
 PATHS = {"blockwise": 0, "sequential": GDN_PATH_SEQUENTIAL, "auto": GDN_PATH_AUTO}
+
+
+class DecodeLayer(ctypes.Structure):
+    """gdn_decode_layer: one layer's device pointers for gdn_decode_step_layers."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "k", "v", "g", "beta", "state_in",
+                                               "state_out", "o")]
 
 
 class GdnError(RuntimeError):
@@ -58,6 +64,8 @@ def lib():
         for fn in ("gdn_decode_step", "gdn_decode_step_qknorm"):
             getattr(L, fn).argtypes = [P] * 8 + [I] * 6 + [P]
             getattr(L, fn).restype = I
+        L.gdn_decode_step_layers.argtypes = [P, I, I, I, I, I, I, I, ctypes.c_uint, P]
+        L.gdn_decode_step_layers.restype = I
         L.gdn_prefill_noalloc.argtypes = [P] * 8 + [I] * 8 + [P]
         L.gdn_prefill_noalloc.restype = I
         L.gdn_prefill_ex.argtypes = [P] * 8 + [I] * 8 + [P, Z, P, ctypes.c_uint]
@@ -226,6 +234,36 @@ def _decode_call(fn, q, k, v, g, beta, state_in, state_out, o, stream):
                             _ptr(state_out), _ptr(o), B, Hk, Hv, dk, dv, dt, _stream(stream))
     if rc != 0:
         raise GdnError(fn, rc)
+
+
+def gdn_decode_step_layers(layers, qk_norm=False, stream=None):
+    """Calls gdn_decode_step_layers: one decode token through independent layers in one launch
+    (per 32 layers).  ``layers``: a list of (q, k, v, g, beta, state_in, state_out, o) tensor
+    tuples, each as for gdn_decode_step, all with the same sizes and dtype."""
+    if not layers:
+        raise ValueError("no layers")
+    q0, v0 = layers[0][0], layers[0][2]
+    B, Hk, dk = q0.shape
+    Hv, dv = v0.shape[1], v0.shape[2]
+    dt = _dt(q0)
+    table = (DecodeLayer * len(layers))()
+    for i, (q, k, v, g, beta, si, so, o) in enumerate(layers):
+        for t in (k, v, o):
+            if _dt(t) != dt:
+                raise TypeError("q, k, v and o must share one dtype")
+        for t, nm in ((g, "g"), (beta, "beta"), (si, "state_in"), (so, "state_out")):
+            _f32(t, nm)
+        if tuple(q.shape) != (B, Hk, dk) or tuple(k.shape) != (B, Hk, dk) or \
+                tuple(v.shape) != (B, Hv, dv) or tuple(o.shape) != (B, Hv, dv) or \
+                tuple(g.shape) != (B, Hv) or tuple(beta.shape) != (B, Hv) or \
+                tuple(si.shape) != (B, Hv, dv, dk) or tuple(so.shape) != (B, Hv, dv, dk):
+            raise ValueError(f"layer {i}: inconsistent shapes")
+        table[i] = DecodeLayer(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(si), _ptr(so),
+                               _ptr(o))
+    rc = lib().gdn_decode_step_layers(table, len(layers), B, Hk, Hv, dk, dv, dt,
+                                      GDN_QK_NORM if qk_norm else 0, _stream(stream))
+    if rc != 0:
+        raise GdnError("gdn_decode_step_layers", rc)
 
 
 # -- conveniences that allocate outputs with torch --------------------------------------------

@@ -161,6 +161,40 @@ def test_decode_rejects(kw, code, fn):
     assert _decode(fn=fn, **kw) == code
 
 
+def _layers(n, **kw):
+    # n layers of fake, well-separated buffers (64 MB apart); kw overrides fields of layer 1
+    T = (gdn.DecodeLayer * n)()
+    for i in range(n):
+        b = BASE + i * 64 * MB
+        T[i] = gdn.DecodeLayer(b, b + MB, b + 2 * MB, b + 3 * MB, b + 4 * MB, b + 10 * MB,
+                               b + 10 * MB, b + 30 * MB)
+    for f, val in kw.items():
+        setattr(T[1], f, val)
+    return T
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(o=None), 1),
+    (dict(k=BASE + 64 * MB + MB + 4), 4),
+    (dict(o=BASE + 64 * MB + 2 * MB), 5),                   # o overlaps its own v
+    (dict(state_out=BASE + 10 * MB), 5),                     # writes layer 0's state
+    (dict(o=BASE + 2 * MB), 5),                              # writes over layer 0's v
+    (dict(state_in=BASE + 30 * MB, state_out=BASE + 64 * MB + 10 * MB), 5),   # reads layer 0's o
+])
+def test_decode_layers_rejects(kw, code):
+    L = gdn.lib()
+    assert L.gdn_decode_step_layers(_layers(3, **kw), 3, 1, 2, 4, 32, 32, 0, 0, None) == code
+
+
+def test_decode_layers_rejects_bad_calls():
+    L = gdn.lib()
+    assert L.gdn_decode_step_layers(None, 3, 1, 2, 4, 32, 32, 0, 0, None) == 1
+    assert L.gdn_decode_step_layers(_layers(3), 0, 1, 2, 4, 32, 32, 0, 0, None) == 2
+    assert L.gdn_decode_step_layers(_layers(3), 3, 1, 2, 5, 32, 32, 0, 0, None) == 2
+    assert L.gdn_decode_step_layers(_layers(3), 3, 1, 2, 4, 48, 32, 0, 0, None) == 3
+    assert L.gdn_decode_step_layers(_layers(3), 3, 1, 2, 4, 32, 32, 0, 2, None) == 3
+
+
 def test_python_binding_raises_with_status():
     with pytest.raises(gdn.GdnError) as ei:
         raise gdn.GdnError("gdn_prefill", 5)
