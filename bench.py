@@ -5,23 +5,25 @@ One step = one pass over the whole hot path on synthetic inputs already resident
 in GPU memory:
   * a blockwise prefill of T = 4096 tokens (B = 1, 16 query/key heads shared 2:1 by
     32 value heads, dk = dv = 128, chunk 64, bf16 q/k/v/o, fp32 gates and state,
-    zero starting state): one gdn_prefill call (both kernels back to back), timed with
-    HIP events on its stream;
+    zero starting state): one gdn_prefill call (both kernels back to back);
   * one decode token through 30 independent recurrent layers (fp32 states of
-    32 x 128 x 128, N(0, 0.1^2)), as 30 back-to-back B = 1 gdn_decode_step calls.
-    The decode is also timed as a captured HIP graph of those 30 launches (no host
-    gaps between layers) and as one B = 30 launch.
-Before every step (outside the timed region) a 1 GiB scratch buffer is written, so
-each step starts with the L2 and the 256 MB last-level cache holding none of its data,
-and inputs also rotate over several buffer sets.
+    32 x 128 x 128, N(0, 0.1^2), each layer's tensors in allocations of their own): one
+    gdn_decode_step_layers launch over the layers' pointer table.
+The K timed steps run back to back on one stream.  The inputs rotate over several buffer
+sets whose total (~1.9 GB) is far larger than the 256 MB last-level cache, so every step
+finds its data in HBM.
 
-value = prefill tokens per second (T / mean event time of the gdn_prefill call).  The
-two kernels are also timed on their own, as the two stages (gdn_prefill_prepare, then
-gdn_prefill_scan) with an event between them, in a separate cold loop: that event adds a
-few microseconds between the kernels, so the split is a breakdown, not the headline.  The
-JSON line also carries the decode figures, the roofline of the prefill path and of the
-decode kernel, and the CPU oracle timed on the host on the same prefill workload (whose
-output doubles as a parity check of the GPU output).
+value = prefill tokens per second: T / the mean duration of one gdn_prefill call, measured
+with HIP events on the stream around spans of K calls enqueued back to back over the same
+rotation (so the figure is the calls' own average, not the cost of an event pair around a
+single launch).  The decode figures are measured the same way: the pointer-table launch (the
+decode roofline), one B = 30 launch over states stored back to back, 30 B = 1 launches, and
+the 30 launches captured in a HIP graph.  Secondary: the same prefill call alone right after
+a 1 GiB flush fill (one call between two events), the two kernels timed as the two stages
+(gdn_prefill_prepare, then gdn_prefill_scan) with an event between them, warm-cache stages,
+the fused-normalisation and all-fp32 calls, and a plain device copy as the achievable-
+bandwidth reference.  The CPU oracle runs on the host on the same prefill workload,
+alternating with cold GPU calls (its output doubles as a parity check of the GPU output).
 """
 import argparse
 import hashlib
@@ -306,34 +308,76 @@ def main():
             raise gdn.GdnError(fn, rc)
 
     nsteps = args.warmup + args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nsteps)]
-    # Written before every step, outside the timed region: evicts the L2 and the 256 MB
-    # last-level cache (the step starts cold), and keeps the GPU busy while the host enqueues
-    # the step, so the events bracket device time only, not host launch gaps.
+    # Written before the single-call cold measurements below (outside their timed spans): it
+    # evicts the L2 and the 256 MB last-level cache.
     scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
 
-    def step(i):
-        j = i % len(sets)
-        e = ev[i]
-        scratch.fill_(i & 0xFF)
-        e[0].record(stream)
-        check(lib.gdn_prefill(*PF[j]), "gdn_prefill")
-        e[1].record(stream)
-        for a in DEC[j]:
-            check(lib.gdn_decode_step(*a), "gdn_decode_step")
-        e[2].record(stream)
+    def prefill_call(i):
+        check(lib.gdn_prefill(*PF[i % len(sets)]), "gdn_prefill")
 
+    def decode_layers(i):
+        check(lib.gdn_decode_step_layers(DEC_L[i % len(sets)], LAYERS, 1, Hk, Hv, dk, dv,
+                                         gdn.GDN_BF16, 0, sh), "gdn_decode_step_layers")
+
+    def decode_batched(i):
+        check(lib.gdn_decode_step(*DEC_B[i % len(sets)]), "gdn_decode_step")
+
+    def decode_looped(i):
+        for a in DEC[i % len(sets)]:
+            check(lib.gdn_decode_step(*a), "gdn_decode_step")
+
+    def span_us(fn, n, start=0):
+        """Mean device time of one fn(i), for n calls enqueued back to back on the stream between
+        two events (i = start .. start + n - 1, rotating over the buffer sets), in us."""
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(start, start + n):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    def step(i):
+        prefill_call(i)
+        decode_layers(i)
+
+    # The K timed steps of the whole hot path -- one prefill call and one decode token through
+    # the 30 layers each -- back to back on one stream.  The inputs rotate over `sets` buffer
+    # sets (~180 MB of prefill data and ~130 MB of decode state each, ~1.9 GB in all), so every
+    # step finds its data in HBM, not in the 256 MB last-level cache.
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev_a.record(stream)
     for i in range(args.warmup, nsteps):
         step(i)
+    ev_b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    timed = ev[args.warmup:]
-    t_prefill = np.array([e[0].elapsed_time(e[1]) for e in timed]) * 1e3   # us
-    t_dec = np.array([e[1].elapsed_time(e[2]) for e in timed]) * 1e3
+    step_us = ev_a.elapsed_time(ev_b) * 1e3 / args.steps
+
+    # Each path's average launch duration, over the same rotation: the prefill call alone and
+    # the decode token alone, n back to back (the headline figures)
+    pf_spans = [span_us(prefill_call, args.steps, r * args.steps) for r in range(3)]
+    t_dec_l = np.array([span_us(decode_layers, args.steps, r * args.steps) for r in range(3)])
+    t_dec_b = np.array([span_us(decode_batched, args.steps, r * args.steps) for r in range(3)])
+    t_dec = np.array([span_us(decode_looped, args.steps, r * args.steps) for r in range(3)])
+
+    # The same prefill call on its own, cold: the flush fill, then one call between two events
+    # (includes the event pair's own cost around a single launch; secondary)
+    t_prefill_single = []
+    for i in range(args.steps + 1):
+        scratch.fill_(i & 0xFF)
+        a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        prefill_call(i)
+        b2.record(stream)
+        torch.cuda.synchronize()
+        if i:
+            t_prefill_single.append(a.elapsed_time(b2) * 1e3)
+    t_prefill_single = np.array(t_prefill_single)
 
     # -- the two prefill kernels on their own, cold: the stages with an event between them --
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -352,33 +396,6 @@ def main():
     t_intra = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
     t_inter = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
 
-    # -- decode, all 30 layers as one batched launch (layers are independent) -------------------
-    evb = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for i in range(args.steps + 3):
-        j = i % len(sets)
-        if i >= 3:
-            evb[i - 3][0].record(stream)
-        check(lib.gdn_decode_step(*DEC_B[j]), "gdn_decode_step")
-        if i >= 3:
-            evb[i - 3][1].record(stream)
-    torch.cuda.synchronize()
-    t_dec_b = np.array([a.elapsed_time(b) for a, b in evb]) * 1e3
-
-    # -- decode, one launch over a pointer table of the 30 separately allocated layers -----------
-    evl = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for i in range(args.steps + 3):
-        j = i % len(sets)
-        if i >= 3:
-            evl[i - 3][0].record(stream)
-        check(lib.gdn_decode_step_layers(DEC_L[j], LAYERS, 1, Hk, Hv, dk, dv, gdn.GDN_BF16, 0, sh),
-              "gdn_decode_step_layers")
-        if i >= 3:
-            evl[i - 3][1].record(stream)
-    torch.cuda.synchronize()
-    t_dec_l = np.array([a.elapsed_time(b) for a, b in evl]) * 1e3
-
     # -- decode as a HIP graph: the 30 sequential launches captured once per buffer set and
     # replayed (no host launch gaps between layers); cold like the main steps ----------------
     cap = torch.cuda.Stream()
@@ -391,17 +408,8 @@ def main():
                 check(lib.gdn_decode_step(*(a[:-1] + (hs,))), "gdn_decode_step")
         graphs.append(g)
     torch.cuda.synchronize()
-    evg = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for i in range(args.steps + 2):
-        scratch.fill_(i & 0xFF)
-        if i >= 2:
-            evg[i - 2][0].record(stream)
-        graphs[i % len(sets)].replay()
-        if i >= 2:
-            evg[i - 2][1].record(stream)
-    torch.cuda.synchronize()
-    t_dec_g = np.array([a.elapsed_time(b) for a, b in evg]) * 1e3
+    t_dec_g = np.array([span_us(lambda i: graphs[i % len(sets)].replay(), args.steps, r * args.steps)
+                        for r in range(3)])
     del graphs
 
     # -- warm-cache prefill (same buffers every time), secondary -------------------------------
@@ -470,7 +478,7 @@ def main():
     copy_gbs = 2 * COPY_CALIBRATION_BYTES / (min(copy_ms) * 1e-3) / 1e9
     del src, dst
 
-    mean_pf = float(t_prefill.mean())
+    mean_pf = float(np.mean(pf_spans))
     value = T / (mean_pf * 1e-6)
     pf_bytes = T * PREFILL_BYTES_PER_TOKEN + STATE_BYTES        # zero start state: state_out only
     pf_flops = T * Hv * PREFILL_FLOP_PER_TOKEN_HEAD
@@ -506,10 +514,16 @@ def main():
         "config": {"workload": w.name, "B": B, "T": T, "Hk": Hk, "Hv": Hv, "dk": dk, "dv": dv,
                    "chunk": C, "state": "fp32, zero start", "decode_layers": LAYERS,
                    "input_sets": args.sets},
+        "step_us": round(step_us, 2),
         "prefill": {
-            "us_mean": round(mean_pf, 2), "us_median": round(float(np.median(t_prefill)), 2),
-            "us_p10": round(float(np.percentile(t_prefill, 10)), 2),
-            "us_p90": round(float(np.percentile(t_prefill, 90)), 2),
+            "us_mean": round(mean_pf, 2),
+            "us_spans": [round(x, 2) for x in pf_spans],
+            "timing": f"mean over {len(pf_spans)} spans of {args.steps} calls enqueued back to back "
+                      f"between two events on the stream, inputs rotating over {args.sets} buffer "
+                      f"sets (each call finds its data in HBM)",
+            "us_single_call_cold_mean": round(float(t_prefill_single.mean()), 2),
+            "us_single_call_cold_p10": round(float(np.percentile(t_prefill_single, 10)), 2),
+            "us_single_call_cold_p90": round(float(np.percentile(t_prefill_single, 90)), 2),
             "intra_chunk_us": round(float(t_intra.mean()), 2),
             "inter_chunk_us": round(float(t_inter.mean()), 2),
             "split_sum_us": round(float((t_intra + t_inter).mean()), 2),
@@ -521,8 +535,8 @@ def main():
             "mfma_frac": round(pf_flops / (mean_pf * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         },
         "roofline": {
-            "kernel": "gdn_prefill = intra_chunk_kernel then inter_chunk_kernel (one call, "
-                      "mean event-timed duration)",
+            "kernel": "gdn_prefill = intra_chunk_kernel then inter_chunk_kernel (mean duration "
+                      "of one call over back-to-back calls, HIP events on the stream)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": pf_bytes,
