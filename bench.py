@@ -173,6 +173,9 @@ def parse():
                     help="time the token-sequential and the blockwise prefill on prefixes of the "
                          "128K long-memory draw (cold, 16/32 heads, d=128, bf16), print one JSON "
                          "line, then exit")
+    ap.add_argument("--crossover-table", action="store_true",
+                    help="time both prefill forms at short prompt lengths for several (dtype, d, "
+                         "heads), print the measured crossovers as one JSON line, then exit")
     return ap.parse_args()
 
 
@@ -229,6 +232,80 @@ def crossover(args):
                                                                  torch.bfloat16)}}), flush=True)
 
 
+# (dtype, d, Hk, Hv, B) of the crossover table; prompt lengths around the crossover
+CROSSOVER_TABLE_CONFIGS = [("bf16", 128, 16, 32, 1), ("f32", 128, 16, 32, 1), ("bf16", 64, 16, 32, 1),
+                           ("f32", 64, 16, 32, 1), ("bf16", 32, 16, 32, 1), ("f32", 32, 16, 32, 1),
+                           ("bf16", 128, 2, 4, 1), ("f32", 128, 2, 4, 1), ("bf16", 128, 16, 32, 4),
+                           ("f32", 128, 16, 32, 4), ("bf16", 64, 16, 32, 4)]
+CROSSOVER_TABLE_T = (1, 8, 16, 24, 32, 40, 48, 56, 64, 80, 96, 128, 160, 192, 256)
+
+
+def crossover_table(args):
+    """The prompt length up to which the token-sequential form beats the blockwise one, per
+    (dtype, d = dk = dv, heads): both forms timed cold on one seeded draw of each shape."""
+    import numpy as np
+    import torch
+
+    from linear_recurrent_attention_gated_amd import gdn
+    from linear_recurrent_attention_gated_amd.inputs import make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    C = 64
+    rows = []
+    for name, d, Hk, Hv, Bt in CROSSOVER_TABLE_CONFIGS:
+        dt = torch.bfloat16 if name == "bf16" else torch.float32
+        Tm = max(CROSSOVER_TABLE_T)
+        full = {k: v.to(dev) for k, v in make_inputs(Bt, Tm, Hk, Hv, d, d, 5, dt).items() if v is not None}
+        ws = torch.empty(gdn.gdn_prefill_workspace_bytes(Bt, Tm, Hk, Hv, d, d, C, dt), dtype=torch.uint8,
+                         device=dev)
+        s_out = torch.empty((Bt, Hv, d, d), dtype=torch.float32, device=dev)
+        points = []
+        for T in CROSSOVER_TABLE_T:
+            x = {k: v[:, :T].contiguous() for k, v in full.items()}
+            o = torch.empty((Bt, T, Hv, d), dtype=dt, device=dev)
+            res = {"T": T}
+            for path, flags in (("sequential", gdn.GDN_PATH_SEQUENTIAL), ("blockwise", 0)):
+                ts = []
+                for r in range(8):
+                    scratch.fill_(r & 0xFF)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    gdn.gdn_prefill_ex(x["q"], x["k"], x["v"], x["g"], x["beta"], None, o, s_out, C, ws,
+                                       flags)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    if r:
+                        ts.append(e0.elapsed_time(e1) * 1e3)
+                res[path + "_us"] = round(float(np.median(ts)), 2)
+            points.append(res)
+        faster = [pt["T"] for pt in points if pt["sequential_us"] < pt["blockwise_us"]]
+        # the crossover: the last length before the first one at which blockwise wins
+        cross = 0
+        for pt in points:
+            if pt["sequential_us"] < pt["blockwise_us"]:
+                cross = pt["T"]
+            else:
+                break
+        # interpolated crossing of the two times between the last length the sequential form
+        # wins and the next
+        x = None
+        for a, b in zip(points, points[1:]):
+            da, db = a["sequential_us"] - a["blockwise_us"], b["sequential_us"] - b["blockwise_us"]
+            if da < 0 <= db:
+                x = round(a["T"] + (b["T"] - a["T"]) * (-da) / (db - da), 1)
+                break
+        row = {"dtype": name, "d": d, "Hk": Hk, "Hv": Hv, "B": Bt, "crossover_T": cross,
+               "crossing_interpolated": x, "sequential_faster_at": faster, "points": points,
+               "auto_max_tokens": gdn.gdn_prefill_sequential_max_tokens(Bt, Hk, Hv, d, d, dt)}
+        rows.append(row)
+        print("[crossover-table]", json.dumps({k: v for k, v in row.items() if k != "points"}),
+              file=sys.stderr, flush=True)
+        del full, ws
+    print(json.dumps({"crossover_table": rows}), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -236,6 +313,9 @@ def main():
         return
     if args.crossover:
         crossover(args)
+        return
+    if args.crossover_table:
+        crossover_table(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the gated-delta-rule core is built and measured "

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
 #include <mutex>
 
 #include "../../include/gdn.h"
@@ -27,9 +28,26 @@ bool overlap(Span a, Span b) {
 }
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Longest prompt for which GDN_PATH_AUTO takes the token-sequential path: measured crossover
-// of the two prefill forms on MI355X at 16 key / 32 value heads, dk = dv = 128, bf16.
-constexpr int kSequentialMaxTokens = 44;
+// Longest prompt for which GDN_PATH_AUTO takes the token-sequential path: the crossover of the
+// two prefill forms measured on MI355X (cold calls, chunk 64), where their times cross.
+//   dk = dv:        32     64    128
+//   bf16 operands:  24     27     45      (the same at 4 and 32 value heads, batch 1)
+//   fp32 operands:  63     96    147
+// The token-sequential form holds a state row on dk / 8 lanes; up to 1,024 waves (one per
+// SIMD) its time per token does not depend on the rows, and the crossover does not either.
+// Above that its time grows with the rows while the blockwise form's short-prompt time barely
+// does: at batch 4, 32 value heads, d = 128 (4,096 waves) the crossings were 25 (bf16) and 56
+// (fp32), a power law in the waves with exponents 0.42 and 0.70.  Between the tabulated
+// dk * dv the crossover is interpolated in log2(dk * dv).
+int sequential_max_tokens(int B, int Hv, int dk, int dv, gdn_dtype dtype) {
+    static const double kBf16[3] = {24.0, 27.0, 45.0}, kF32[3] = {63.0, 96.0, 147.0};
+    const double* t = dtype == GDN_BF16 ? kBf16 : kF32;
+    const double x = std::log2((double)dk * dv);   // 10 .. 14
+    double t1 = x <= 12.0 ? t[0] + (t[1] - t[0]) * (x - 10.0) / 2.0 : t[1] + (t[2] - t[1]) * (x - 12.0) / 2.0;
+    const double waves = (double)B * Hv * dv * (dk / 8) / 64.0;
+    if (waves > 1024.0) t1 *= std::pow(1024.0 / waves, dtype == GDN_BF16 ? 0.42 : 0.70);
+    return t1 < 1.0 ? 1 : (int)t1;
+}
 
 // Workspace regions of the blockwise prefill (see gdn_prefill.h).
 struct Layout {
@@ -235,8 +253,8 @@ gdn_status gdn_prefill_ex(const void* q, const void* k, const void* v, const flo
 }
 
 int gdn_prefill_sequential_max_tokens(int B, int Hk, int Hv, int dk, int dv, gdn_dtype dtype) {
-    (void)B; (void)Hk; (void)Hv; (void)dk; (void)dv; (void)dtype;
-    return kSequentialMaxTokens;
+    if (shape_check(B, 1, Hk, Hv, dk, dv, 16, dtype, true) != GDN_OK) return 0;
+    return sequential_max_tokens(B, Hv, dk, dv, dtype);
 }
 
 gdn_status gdn_prefill_qknorm(const void* q, const void* k, const void* v, const float* g,
