@@ -11,7 +11,7 @@
 //   B (K x 16): col  l % 16, k = (l / 16) * KPL + [0, KPL)
 //   D (16 x 16): col l % 16, rows (l / 16) * 4 + [0, 4)
 // Operands read from memory laid out contiguous along k are one 16-byte load per bf16
-// fragment and one 4-byte load per fp32 fragment.
+// fragment and per four fp32 fragments (Elem::GRP).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -103,6 +103,14 @@ template <> struct Elem<bf16_t> {
     __device__ static __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
+    // Fragments in 16-byte lane groups (see the fp32 traits): a bf16 fragment is one group.
+    static constexpr int GRP = 1;
+    __device__ static __forceinline__ int doff(int kb, int g) { return kb * 32 + g * 8; }
+    __device__ static __forceinline__ int foff(int kb, int lane) { return (kb * 64 + lane) * 8; }
+    __device__ static __forceinline__ void ld_grp(const bf16_t* p, frag* f) { f[0] = ld(p); }
+    __device__ static __forceinline__ void st_grp(bf16_t* p, const frag* f) {
+        *reinterpret_cast<uint4*>(p) = __builtin_bit_cast(uint4, f[0]);
+    }
 };
 
 template <> struct Elem<float> {
@@ -122,6 +130,24 @@ template <> struct Elem<float> {
     __device__ static __forceinline__ frag keep_if(frag a, bool keep) { return keep ? a : 0.0f; }
     __device__ static __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    // An fp32 fragment is 4 bytes per lane, so operands are moved four fragments at a time:
+    //   doff(kb, g)    offset in a row contiguous along k of fragment kb's element for lane
+    //                  group g.  Products over dk use the permuted order here too, so that
+    //                  fragments 4j..4j+3 of a lane are 4 consecutive row elements;
+    //   foff(kb, lane) offset of fragment kb's lane element in an array of stored fragments:
+    //                  fragments 4j..4j+3 of a lane are adjacent (one 16-byte piece per lane).
+    static constexpr int GRP = 4;
+    __device__ static __forceinline__ int doff(int kb, int g) { return poff(kb, g); }
+    __device__ static __forceinline__ int foff(int kb, int lane) {
+        return ((kb >> 2) * 64 + lane) * 4 + (kb & 3);
+    }
+    __device__ static __forceinline__ void ld_grp(const float* p, frag* f) {
+        const float4 v = *reinterpret_cast<const float4*>(p);
+        f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+    }
+    __device__ static __forceinline__ void st_grp(float* p, const frag* f) {
+        *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
     }
 };
 

@@ -41,9 +41,11 @@
 // Workspace layout (E = element type; a fragment is 64 lanes x KPL elements of a 16 x KB
 // operand tile, lane l holding row l % 16).  Fragments marked "permuted" hold, in lane group
 // g = l / 16, the k-values Elem<E>::kperm(kb, g, 0..KPL-1) of k-block kb; the others hold
-// k = kb * KB + g * KPL + [0, KPL).  The permuted order is the one an accumulator tile
-// provides without lane exchanges (see gdn_device.h), and the scan reads the matching
-// operand in the same order.
+// k = Elem<E>::doff(kb, g) + [0, KPL) (bf16: kb * KB + g * KPL; fp32: the permuted order as
+// well).  The permuted order is the one an accumulator tile provides without lane exchanges
+// (see gdn_device.h), and the scan reads the matching operand in the same order.  Fragment f
+// of an array stands at Elem<E>::foff(f, lane): bf16 fragments one after another, fp32 ones in
+// groups of four whose lane elements are adjacent, so every lane moves 16 bytes at a time.
 //   KF  [B][Hk][N][C/16][DK/KB] fragments   A operand of K S^T   (rows tokens, k = dk) -- the raw k
 //       rows (zero past the chunk's end), so the scan reads them contiguously
 //   QF  [B][Hk][N][C/16][DK/KB] fragments   A operand of Q S^T   (rows tokens, k = dk) -- the raw q
@@ -184,6 +186,8 @@ __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
 // NORM: q and k are L2-normalised (p.qk_norm); a separate instantiation, so that the plain
 // path carries none of its registers.
 template <typename E, int DK, int DV, int C, bool NORM>
+// Two workgroups per CU in both builds: the fp32 one (69 KB of LDS without the K^T copy) then
+// spills a few registers, and still runs ~25% faster than with one workgroup per CU.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void intra_chunk_kernel(PrefillParams p) {
     using S = PrefillShape<E, DK, DV, C>;
     using X = Elem<E>;
@@ -203,7 +207,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     auto kb_lo = [](int kb) { return kb * KB / KSPAN * KSPAN; };
 
     __shared__ __align__(16) E Ks[C * LDK];
-    __shared__ __align__(16) E KsT[DK * LDT];
+    // token-contiguous K^T rows: the B operand of phase 4 needs 8 consecutive tokens of one dk
+    // column per lane in bf16; an fp32 fragment is one element per lane, read from Ks directly
+    constexpr bool TRK = KPL == 8;
+    __shared__ __align__(16) E KsT[TRK ? DK * LDT : 4];
     __shared__ __align__(16) float sR[C * LDR];    // A, then R in place
     __shared__ __align__(16) float sRT[C * LDR];   // row s: beta_s R[r][s] for r < CP (zero past C)
     __shared__ __align__(16) float sg2[C];         // gamma * log2(e)
@@ -297,9 +304,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     auto load_q = [&](const Item& it) {
         const int t0 = it.c * C, n = min(C, T - t0);
         const E* qg = reinterpret_cast<const E*>(p.q) + ((size_t)it.b * p.Ts + p.t0 + t0) * rsk + (size_t)(it.h / grp) * DK;
-        const E* src = qg + (size_t)min(pm_ld * 16 + rl, n - 1) * rsk + kq;
+        const E* src = qg + (size_t)min(pm_ld * 16 + rl, n - 1) * rsk;
 #pragma unroll
-        for (int kb = 0; kb < NKD; ++kb) qf[kb] = X::ld(src + kb * KB);
+        for (int kb = 0; kb < NKD; kb += X::GRP) X::ld_grp(src + X::doff(kb, g), &qf[kb]);
     };
 
     int item = blockIdx.x;
@@ -343,15 +350,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 sk2p[(r0 + i) * (VKN + 1) + cv] = ss;
             }
         }
+        if constexpr (TRK) {
 #pragma unroll
-        for (int j = 0; j < EPV; ++j) {
-            E run[8];
+            for (int j = 0; j < EPV; ++j) {
+                E run[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) run[i] = el[i < PK ? i : 0][j];
-            store_run(KsT + (cv * EPV + j) * LDT + r0, run, PK);
+                for (int i = 0; i < 8; ++i) run[i] = el[i < PK ? i : 0][j];
+                store_run(KsT + (cv * EPV + j) * LDT + r0, run, PK);
+            }
         }
     }
-    if (CP > C) {   // token columns past the chunk (16-token chunks in bf16)
+    if (TRK && CP > C) {   // token columns past the chunk (16-token chunks in bf16)
         for (int e = tid; e < DK * (CP - C); e += kThreads) {
             const int d = e / (CP - C), s = C + e % (CP - C);
             KsT[d * LDT + s] = X::from_f(0.f);
@@ -432,11 +441,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
     // Gram tile of K rows: D[r][s] = k_r . k_s  (r in tile tm, s in tile tn)
     auto kk_tile = [&](int tm, int tn) {
-        const E* ar = Ks + (tm * 16 + rl) * LDK + kq;
-        const E* br = Ks + (tn * 16 + rl) * LDK + kq;
+        const E* ar = Ks + (tm * 16 + rl) * LDK;
+        const E* br = Ks + (tn * 16 + rl) * LDK;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int kb = 0; kb < NKD; ++kb) acc = X::mma(X::ld(ar + kb * KB), X::ld(br + kb * KB), acc);
+        for (int kb = 0; kb < NKD; kb += X::GRP) {
+            frag a[X::GRP], bb[X::GRP];
+            X::ld_grp(ar + X::doff(kb, g), a);
+            X::ld_grp(br + X::doff(kb, g), bb);
+#pragma unroll
+            for (int i = 0; i < X::GRP; ++i) acc = X::mma(a[i], bb[i], acc);
+        }
         return acc;
     };
     // A[r][s] = beta_r exp(gamma_r - gamma_s) (k_r . k_s) for s < r, from a Gram tile
@@ -462,9 +477,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         auto ptile = [&](int t) {
             f32x4 acc = zero4();
             if (t <= m) {
-                const E* ar = Ks + (t * 16 + rl) * LDK + kq;
+                const E* ar = Ks + (t * 16 + rl) * LDK;
 #pragma unroll
-                for (int kb = 0; kb < NKD; ++kb) acc = X::mma(X::ld(ar + kb * KB), qf[kb], acc);
+                for (int kb = 0; kb < NKD; kb += X::GRP) {
+                    frag a[X::GRP];
+                    X::ld_grp(ar + X::doff(kb, g), a);
+#pragma unroll
+                    for (int i = 0; i < X::GRP; ++i) acc = X::mma(a[i], qf[kb + i], acc);
+                }
                 const float4 gs = *reinterpret_cast<const float4*>(sg2 + t * 16 + rq);
                 const float4 ks = invk4(t * 16 + rq);
                 const float gsv[4] = {gs.x, gs.y, gs.z, gs.w}, ksv[4] = {ks.x, ks.y, ks.z, ks.w};
@@ -497,12 +517,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const size_t off = (((size_t)b * Hk + hk) * N + c) * S::W_PER_CHUNK;
         E* KFg = reinterpret_cast<E*>(p.KF) + off;
         E* QFg = reinterpret_cast<E*>(p.QF) + off;
-        const E* krow = Ks + (m * 16 + rl) * LDK + kq;
+        const E* krow = Ks + (m * 16 + rl) * LDK;
+        const size_t tile = (size_t)m * NKD * 64 * KPL;   // (NKD is a multiple of the group)
 #pragma unroll
-        for (int kb = 0; kb < NKD; ++kb) {
-            const size_t f = ((size_t)(m * NKD + kb) * 64 + lane) * KPL;
-            *reinterpret_cast<frag*>(KFg + f) = X::ld(krow + kb * KB);
-            *reinterpret_cast<frag*>(QFg + f) = qf[kb];
+        for (int kb = 0; kb < NKD; kb += X::GRP) {
+            const size_t f = tile + X::foff(kb, lane);
+            *reinterpret_cast<uint4*>(KFg + f) = *reinterpret_cast<const uint4*>(krow + X::doff(kb, g));
+            X::st_grp(QFg + f, &qf[kb]);
         }
     };
 
@@ -657,13 +678,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
         E* Zg = reinterpret_cast<E*>(p.Z) + (bh * N + c) * S::Z_PER_CHUNK;
         for (int dt = wave / NG; dt < ND; dt += 4 / NG) {
-            const E* br = KsT + (dt * 16 + rl) * LDT + kq;
+            // B operand: K^T rows (dk) over tokens -- from KsT (bf16) or a column of Ks (fp32)
+            auto kt = [&](int kb) {
+                if constexpr (TRK) return X::ld(KsT + (dt * 16 + rl) * LDT + kq + kb * KB);
+                else return X::ld(Ks + (kb * KB + kq) * LDK + dt * 16 + rl);
+            };
             f32x4 acc[TPG];
 #pragma unroll
             for (int i = 0; i < TPG; ++i) acc[i] = zero4();
 #pragma unroll
             for (int kb = 0; kb < NKC; ++kb) {
-                const frag bk = X::ld(br + kb * KB);
+                const frag bk = kt(kb);
 #pragma unroll
                 for (int i = 0; i < TPG; ++i) {
                     const int u = zg * TPG + i;
@@ -672,9 +697,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             }
             if constexpr (KPL == 8) {
                 *reinterpret_cast<frag*>(Zg + ((size_t)(dt * NKC + zg) * 64 + lane) * KPL) = X::pack(acc[0], acc[TPG - 1]);
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) Zg[(size_t)(dt * NKC + 4 * zg + j) * 64 + lane] = acc[0][j];
+            } else {   // fragments 4 zg .. 4 zg + 3: one lane group
+                const frag f[4] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3]};
+                X::st_grp(Zg + (size_t)dt * NKC * 64 * KPL + X::foff(4 * zg, lane), f);
             }
         }
 
@@ -711,8 +736,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                 for (int u = 0; u < NT; ++u) {
                     if (u > m) break;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) Pg[(size_t)(m * NKC + 4 * u + j) * 64 + lane] = acc[u][j];
+                    const frag f[4] = {acc[u][0], acc[u][1], acc[u][2], acc[u][3]};
+                    X::st_grp(Pg + (size_t)m * NKC * 64 * KPL + X::foff(4 * u, lane), f);
                 }
             }
         }
@@ -808,7 +833,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
     const int i0 = slice * 16;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int rl = lane & 15, g = lane >> 4, kq = g * KPL, rq = g * 4;
+    const int rl = lane & 15, g = lane >> 4, rq = g * 4;
     const bool chain = wave < 4;
     const int w4 = wave & 3;
     const bool has_tile = w4 < NT;
@@ -827,7 +852,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
         // the chain is the critical path: its waves win instruction arbitration on their SIMDs
         __builtin_amdgcn_s_setprio(3);
         const E* KFg = reinterpret_cast<const E*>(p.KF) + ((size_t)b * Hk + hk) * N * Sh::W_PER_CHUNK
-                       + ((size_t)m * NKD * 64 + lane) * KPL;
+                       + (size_t)m * NKD * Sh::FRAG;
         const E* Zg = reinterpret_cast<const E*>(p.Z) + (size_t)bh * N * Sh::Z_PER_CHUNK;
         // v of this lane's state row (i0 + rl) for token rows rq + [0, 4) of tile m
         const E* vg = reinterpret_cast<const E*>(p.v) + (size_t)h * DV + i0 + rl;
@@ -841,7 +866,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
             op.gk = *reinterpret_cast<const f32x4*>(gc + C + m * 16 + rq);
             const E* ksrc = KFg + (size_t)c * Sh::W_PER_CHUNK;
 #pragma unroll
-            for (int kb = 0; kb < NKD; ++kb) op.kf[kb] = X::ld(ksrc + kb * Sh::FRAG);
+            for (int kb = 0; kb < NKD; kb += X::GRP) X::ld_grp(ksrc + X::foff(kb, lane), &op.kf[kb]);
         };
         auto fetch_v = [&](E (&v)[4], int c) {
             const int tb = c * C + m * 16 + rq;   // rows past the prompt read its last token
@@ -854,9 +879,9 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
 #pragma unroll
             for (int tw = 0; tw < TPW; ++tw) {
                 const int dt = min(w4 + 4 * tw, DT - 1);
-                const E* zsrc = Zg + (size_t)c * Sh::Z_PER_CHUNK + ((size_t)dt * NKC * 64 + lane) * KPL;
+                const E* zsrc = Zg + (size_t)c * Sh::Z_PER_CHUNK + (size_t)dt * NKC * Sh::FRAG;
 #pragma unroll
-                for (int kb = 0; kb < NKC; ++kb) op.z[tw][kb] = X::ld(zsrc + kb * Sh::FRAG);
+                for (int kb = 0; kb < NKC; kb += X::GRP) X::ld_grp(zsrc + X::foff(kb, lane), &op.z[tw][kb]);
             }
         };
         auto fetch = [&](COps& op, int c) { fetch_w(op, c); fetch_k(op, c); };
@@ -895,13 +920,13 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
             __builtin_amdgcn_sched_barrier(0);
             const int cur = c & 1;
             if (has_tile) {
-                const E* sr = &Sb[cur][rl * LDS_ + kq];
-                const E* sl = &Sl[cur][SPLIT ? rl * LDS_ + kq : 0];
+                const E* sr = &Sb[cur][rl * LDS_];
+                const E* sl = &Sl[cur][SPLIT ? rl * LDS_ : 0];
                 typename X::frag sh[NKD], slo[NKD];
 #pragma unroll
-                for (int kb = 0; kb < NKD; ++kb) {
-                    sh[kb] = X::ld(sr + kb * KB);
-                    if (SPLIT) slo[kb] = X::ld(sl + kb * KB);
+                for (int kb = 0; kb < NKD; kb += X::GRP) {
+                    X::ld_grp(sr + X::doff(kb, g), &sh[kb]);
+                    if (SPLIT) X::ld_grp(sl + X::doff(kb, g), &slo[kb]);
                 }
                 f32x4 acc = zero4(), accl = zero4();
 #pragma unroll
@@ -1002,7 +1027,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
         const E* Pg = reinterpret_cast<const E*>(p.P) + (size_t)bh * N * Sh::P_PER_CHUNK;
         const int pkmax = (m * 16 + 15) / KB;   // last k-block of P row tile m with nonzeros
         const E* qfg = reinterpret_cast<const E*>(p.QF) + ((size_t)b * Hk + hk) * N * Sh::W_PER_CHUNK
-                       + ((size_t)m * NKD * 64 + lane) * KPL;
+                       + (size_t)m * NKD * Sh::FRAG;
         E* og = reinterpret_cast<E*>(p.o) + (size_t)h * DV + i0;
 
         auto fetch = [&](OOps& op, int c) {
@@ -1010,11 +1035,19 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
             op.gr = *reinterpret_cast<const f32x4*>(gates + (size_t)c * Sh::GATES + m * 16 + rq);
             const E* qsrc = qfg + (size_t)c * Sh::W_PER_CHUNK;
 #pragma unroll
-            for (int kb = 0; kb < NKD; ++kb) op.q[kb] = X::ld(qsrc + (size_t)kb * Sh::FRAG);
-            const E* psrc = Pg + (size_t)c * Sh::P_PER_CHUNK + (size_t)m * NKC * Sh::FRAG + lane * KPL;
+            for (int kb = 0; kb < NKD; kb += X::GRP) X::ld_grp(qsrc + X::foff(kb, lane), &op.q[kb]);
+            const E* psrc = Pg + (size_t)c * Sh::P_PER_CHUNK + (size_t)m * NKC * Sh::FRAG;
+            // k-blocks past the diagonal are zero, not stored (an fp32 group of four k-blocks
+            // is one 16-token tile, wholly on one side of it)
 #pragma unroll
-            for (int kb = 0; kb < NKC; ++kb)   // k-blocks past the diagonal are zero, not stored
-                op.p[kb] = kb <= pkmax ? X::ld(psrc + kb * Sh::FRAG) : X::zero();
+            for (int kb = 0; kb < NKC; kb += X::GRP) {
+                if (kb <= pkmax) {
+                    X::ld_grp(psrc + X::foff(kb, lane), &op.p[kb]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < X::GRP; ++i) op.p[kb + i] = X::zero();
+                }
+            }
         };
         auto step = [&](const OOps& op, int c, auto tailtag) {
             constexpr bool TAIL = decltype(tailtag)::value;
@@ -1022,12 +1055,17 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
             const int t0 = c * C;
             lds_barrier();   // (B1) Y of chunk c is in LDS; buffer (c & 1) holds chunk c's slice
             if (has_tile) {
-                const E* sr = &Sb[c & 1][rl * LDS_ + kq];
+                const E* sr = &Sb[c & 1][rl * LDS_];
                 const bool qok = !TAIL || (t0 + m * 16 + rl < T);
                 f32x4 accq = zero4();
 #pragma unroll
-                for (int kb = 0; kb < NKD; ++kb)
-                    accq = X::mma(TAIL ? X::keep_if(op.q[kb], qok) : op.q[kb], X::ld(sr + kb * KB), accq);
+                for (int kb = 0; kb < NKD; kb += X::GRP) {
+                    frag sh[X::GRP];
+                    X::ld_grp(sr + X::doff(kb, g), sh);
+#pragma unroll
+                    for (int i = 0; i < X::GRP; ++i)
+                        accq = X::mma(TAIL ? X::keep_if(op.q[kb + i], qok) : op.q[kb + i], sh[i], accq);
+                }
                 f32x4 acc = accq * op.gr;
 #pragma unroll
                 for (int kb = 0; kb < NKC; ++kb)   // P fragments: tokens in the permuted order

@@ -148,3 +148,37 @@ def test_planted_regrouping_is_caught():
     regroup = lambda wave, NG: (wave // 2, wave % 2, 2)  # noqa: E731
     bad = {(e, c, d) for (e, c, d) in INSTANCES if e == "bf16" and coverage_errors(e, c, d, regroup)}
     assert bad == {("bf16", c, d) for c in (16, 32) for d in (32, 64, 128)}
+
+
+def foff(elem, f, lane):
+    """Offset, in elements, of fragment f's lane element in an array of stored fragments
+    (gdn_device.h, Elem::foff): bf16 fragments of 8 elements one after another; fp32 fragments
+    in groups of four whose lane elements are adjacent."""
+    if elem == "bf16":
+        return (f * 64 + lane) * 8
+    return ((f >> 2) * 64 + lane) * 4 + (f & 3)
+
+
+@pytest.mark.parametrize("elem,C,dk", INSTANCES)
+def test_grouped_fragment_offsets_tile_each_chunk(elem, C, dk):
+    # The stores and loads address fragment f of a tile as tile_base + foff(f, lane), with the
+    # tile bases of the kernels (row tile m of KF/QF: m * NKD fragments; dk tile dt of Z:
+    # dt * NKC; row tile m of P': m * NKC).  Within one chunk the offsets must be a bijection
+    # onto its elements, and a 16-byte lane group must never straddle two tiles.
+    S = shape(elem, C, dk)
+    kpl = 8 if elem == "bf16" else 1
+    grp = 1 if elem == "bf16" else 4
+    for tiles, per_tile in ((S["NT"], S["NKD"]), (S["ND"], S["NKC"]), (S["NT"], S["NKC"])):
+        assert per_tile % grp == 0
+        seen = set()
+        for t in range(tiles):
+            base = t * per_tile * 64 * kpl
+            for f in range(per_tile):
+                for lane in range(64):
+                    o = base + foff(elem, f, lane)
+                    for e in range(kpl):
+                        assert o + e not in seen
+                        seen.add(o + e)
+                    if f % grp:   # adjacent to the group's first fragment
+                        assert o == base + foff(elem, f - f % grp, lane) + f % grp
+        assert seen == set(range(tiles * per_tile * 64 * kpl))
