@@ -169,6 +169,13 @@ def parse():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script "
                          "with --copy-calibration into profiles/hbm_traffic.txt, then exit")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="turn a rocprofv3 --kernel-trace run of this script (with --no-cpu-baseline "
+                         "and the same --steps / --warmup) into the per-phase kernel table in "
+                         "profiles/, then exit")
+    ap.add_argument("--trace-bench-out", metavar="FILE",
+                    help="with --summarize-trace: the profiled run's stdout (its JSON line), to "
+                         "set its event-timed figures beside the kernel times")
     ap.add_argument("--crossover", action="store_true",
                     help="time the token-sequential and the blockwise prefill on prefixes of the "
                          "128K long-memory draw (cold, 16/32 heads, d=128, bf16), print one JSON "
@@ -306,10 +313,133 @@ def crossover_table(args):
     print(json.dumps({"crossover_table": rows}), flush=True)
 
 
+TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_stats_prefill_4k_decode_30layers.md")
+
+
+def summarize_trace(trace_dir, warmup, steps, bench_out=None):
+    """Per-kernel launch durations from a rocprofv3 --kernel-trace run of this script (made with
+    --no-cpu-baseline and the given --warmup / --steps), written to TRACE_FILE.  The launches
+    of each kernel are split into the script's phases by their order in the trace."""
+    import csv
+    import glob
+
+    rows = []
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        sys.exit("no *kernel_trace.csv under " + trace_dir)
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+
+    def dur(r):
+        return (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+
+    def grid(r):
+        return int(float(r.get("Grid_Size_X") or r.get("Grid_Size") or 0))
+
+    def short(n):
+        return n.split("(")[0]
+
+    W, K = warmup, steps
+    by_name, by_shape = {}, {}
+    for r in rows:
+        by_name.setdefault(short(r["Kernel_Name"]), []).append(dur(r))
+        by_shape.setdefault((short(r["Kernel_Name"]), grid(r)), []).append(dur(r))
+    total = sum(sum(v) for v in by_name.values())
+    mean = lambda v: sum(v) / len(v) if v else float("nan")  # noqa: E731
+    out = ["# Kernel time: prefill T=4096 (Hk=16, Hv=32, dk=dv=128, chunk 64) and a 30-layer decode",
+           "",
+           "Command (repo root):",
+           "",
+           "    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/stats -o bench -- \\",
+           "        python bench.py --steps %d --warmup %d --no-cpu-baseline%s" % (
+               K, W, " > " + bench_out if bench_out else ""),
+           "    python bench.py --summarize-trace gpurun_out/stats --steps %d --warmup %d%s" % (
+               K, W, " --trace-bench-out " + bench_out if bench_out else ""),
+           "",
+           "One bench step is one gdn_prefill call (intra_chunk_kernel then inter_chunk_kernel) and",
+           "one gdn_decode_step_layers launch over 30 separately allocated layers, inputs rotating",
+           "over buffer sets that do not fit the last-level cache.  After the steps the script runs,",
+           "in this order: 3 spans of %d prefill calls back to back (the headline), 3 x %d layer" % (K, K),
+           "launches, 3 x %d B=30 decode launches, 3 x %d x 30 B=1 decode launches, %d single cold" % (K, K, K + 1),
+           "prefill calls (flush fill first), %d cold split-stage calls, 3 x %d replays of a HIP graph" % (K + 2, K),
+           "of the 30 B=1 launches, %d warm split-stage calls, 11 cold fused-normalisation calls (their" % (K + 2),
+           "scan is the bf16 inter kernel), 11 cold all-fp32 calls (`float` instances) and a 512 MiB",
+           "device copy.  Averages over all launches of a kernel therefore mix these phases; the",
+           "phase tables below split them.",
+           "",
+           "| Kernel | Calls | Avg (us) | Min (us) | Max (us) | Share |",
+           "|---|---|---|---|---|---|"]
+    for k, v in sorted(by_name.items(), key=lambda kv: -sum(kv[1])):
+        out.append("| %s | %d | %.2f | %.2f | %.2f | %.2f%% |" % (k, len(v), mean(v), min(v), max(v),
+                                                                100 * sum(v) / total))
+    out += ["", "Per launch shape (grid in work-items):", "",
+            "| Kernel | Grid | Calls | Avg (us) | Min (us) | Max (us) |", "|---|---|---|---|---|---|"]
+    for (k, gsz), v in sorted(by_shape.items(), key=lambda kv: -sum(kv[1])):
+        out.append("| %s | %d | %d | %.2f | %.2f | %.2f |" % (k, gsz, len(v), mean(v), min(v), max(v)))
+
+    def seq(pat):
+        return [dur(r) for r in rows if pat in r["Kernel_Name"]]
+
+    intra = seq("intra_chunk_kernel<unsigned short, 128, 128, 64, false>")
+    inter = seq("inter_chunk_kernel<unsigned short, 128, 128, 64, true>")
+    phases = [("timed steps (each call followed by a decode launch)", W, W + K),
+              ("spans of back-to-back calls (headline)", W + K, W + 4 * K),
+              ("single calls, cold", W + 4 * K + 1, W + 5 * K + 1),
+              ("split stages, cold", W + 5 * K + 3, W + 6 * K + 3),
+              ("split stages, warm", W + 6 * K + 5, W + 7 * K + 5)]
+    out += ["", "bf16 prefill kernels by phase (average launch duration, us):", "",
+            "| Phase | Calls | intra_chunk_kernel | inter_chunk_kernel | Sum |", "|---|---|---|---|---|"]
+    for name, a, b in phases:
+        i, j = intra[a:b], inter[a:b]
+        out.append("| %s | %d | %.2f | %.2f | %.2f |" % (name, len(i), mean(i), mean(j), mean(i) + mean(j)))
+    lay = seq("decode_layers_kernel")
+    d30 = [dur(r) for r in rows if "decode_kernel<" in r["Kernel_Name"] and grid(r) == LAYERS * 32 * 8 * 256]
+    d1 = [dur(r) for r in rows if "decode_kernel<" in r["Kernel_Name"] and grid(r) == 32 * 8 * 256]
+    n1 = 3 * K * LAYERS
+    f32i, f32s = seq("intra_chunk_kernel<float"), seq("inter_chunk_kernel<float")
+    out += ["", "Decode and the other prefill builds (average launch duration, us):", "",
+            "| Launch | Calls | Avg (us) |", "|---|---|---|",
+            "| decode_layers_kernel, 30 layers, timed steps | %d | %.2f |" % (len(lay[W:W + K]), mean(lay[W:W + K])),
+            "| decode_layers_kernel, 30 layers, back-to-back spans | %d | %.2f |" % (len(lay[W + K:W + 4 * K]),
+                                                                                 mean(lay[W + K:W + 4 * K])),
+            "| decode_kernel B=30, back-to-back spans | %d | %.2f |" % (len(d30), mean(d30)),
+            "| decode_kernel B=1, eager (30 per token) | %d | %.2f |" % (len(d1[:n1]), mean(d1[:n1])),
+            "| decode_kernel B=1, graph replays | %d | %.2f |" % (len(d1[n1:]), mean(d1[n1:])),
+            "| intra_chunk_kernel, fused normalisation, cold | %d | %.2f |" % (
+                len(seq("intra_chunk_kernel<unsigned short, 128, 128, 64, true>")),
+                mean(seq("intra_chunk_kernel<unsigned short, 128, 128, 64, true>"))),
+            "| intra_chunk_kernel fp32, cold | %d | %.2f |" % (len(f32i), mean(f32i)),
+            "| inter_chunk_kernel fp32, cold | %d | %.2f |" % (len(f32s), mean(f32s))]
+    if bench_out:
+        # the profiled run's own HIP-event figures (its JSON line), against the kernel times
+        doc = None
+        with open(bench_out) as fh:
+            for line in fh:
+                if line.startswith("{") and '"metric"' in line:
+                    doc = json.loads(line)
+        if doc:
+            pf, dec = doc["prefill"], doc["decode"]
+            spans = phases[1]
+            out += ["", "The same (profiled) run's HIP-event figures, from its JSON line: prefill call %.2f us "
+                    "(spans %s) against %.2f us of kernel time in the spans phase above; decode "
+                    "layers launch %.2f us against %.2f us.  Kernel-trace collection slows the "
+                    "launches a little: the default bench run without the profiler is the "
+                    "reference for the headline figures." % (
+                        pf["us_mean"], pf["us_spans"], mean(intra[spans[1]:spans[2]]) + mean(inter[spans[1]:spans[2]]),
+                        dec["us_per_token_layers"], mean(lay[W + K:W + 4 * K]))]
+    with open(TRACE_FILE, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    print(TRACE_FILE)
+
+
 def main():
     args = parse()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.warmup, args.steps, args.trace_bench_out)
         return
     if args.crossover:
         crossover(args)
