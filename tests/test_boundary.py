@@ -144,10 +144,10 @@ def test_sequential_crossover_follows_the_measured_table():
     f = gdn.gdn_prefill_sequential_max_tokens
     # batch 1 at 32 value heads: the measured crossovers (bf16, fp32) x (d = 32, 64, 128)
     assert [f(1, 16, 32, d, d, 0) for d in (32, 64, 128)] == [24, 27, 45]
-    assert [f(1, 16, 32, d, d, 1) for d in (32, 64, 128)] == [63, 96, 147]
+    assert [f(1, 16, 32, d, d, 1) for d in (32, 64, 128)] == [55, 84, 119]
     assert f(1, 2, 4, 128, 128, 0) == 45                   # fewer heads: unchanged
     assert 20 <= f(4, 16, 32, 128, 128, 0) <= 30           # batch 4 measured 25
-    assert 50 <= f(4, 16, 32, 128, 128, 1) <= 60           # batch 4 measured 56
+    assert 43 <= f(4, 16, 32, 128, 128, 1) <= 53           # batch 4 measured 48
     assert 24 < f(1, 16, 32, 64, 128, 0) < 45              # between the tabulated sizes
     assert f(1000, 16, 32, 128, 128, 0) >= 1
     assert f(1, 16, 32, 96, 128, 0) == 0                   # unsupported size
