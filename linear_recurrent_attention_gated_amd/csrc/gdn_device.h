@@ -153,6 +153,23 @@ template <> struct Elem<float> {
 
 __device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
 
+// Makes a register value opaque to the compiler at this point (an empty asm that "modifies"
+// it): nothing derived from it can be computed earlier, and a load that produced it is waited
+// for here at the latest.
+template <typename T>
+__device__ __forceinline__ void reg_fence(T& x) {
+    static_assert(sizeof(T) == 16 || sizeof(T) == 4, "16- or 4-byte values");
+    if constexpr (sizeof(T) == 16) {
+        uint4 u = __builtin_bit_cast(uint4, x);
+        asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
+        x = __builtin_bit_cast(T, u);
+    } else {
+        uint32_t u = __builtin_bit_cast(uint32_t, x);
+        asm volatile("" : "+v"(u));
+        x = __builtin_bit_cast(T, u);
+    }
+}
+
 // Streaming (nontemporal) 16-byte global accesses, for data a launch touches once: they carry
 // the nontemporal cache hint, under which HBM reads and writes stream faster than with the
 // default policy (a plain device copy on MI355X: ~6.2 TB/s with the hint, ~4.9 without).

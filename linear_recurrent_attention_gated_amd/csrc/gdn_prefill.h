@@ -274,6 +274,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     uint32_t vl[NVL] = {};
     uint32_t vsink = 0;
     frag qf[NKD];
+    // bf16: the next item's Q fragments arrive in registers of their own, loaded as phase 2
+    // starts; fp32 (twice the registers) reloads qf once phase 2 is done with it
+    constexpr bool QN = KPL == 8;
+    frag qn[QN ? NKD : 1];
     float graw, braw;
     auto load_kg = [&](const Item& it) {
         const int t0 = it.c * C, n = min(C, T - t0);
@@ -301,19 +305,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             vl[i] = *reinterpret_cast<const uint32_t*>(vg + (size_t)min(r, n - 1) * rsv + ln * (128 / (int)sizeof(E)));
         }
     };
-    auto load_q = [&](const Item& it) {
+    auto load_q = [&](const Item& it, frag (&dst)[NKD]) {
         const int t0 = it.c * C, n = min(C, T - t0);
         const E* qg = reinterpret_cast<const E*>(p.q) + ((size_t)it.b * p.Ts + p.t0 + t0) * rsk + (size_t)(it.h / grp) * DK;
         const E* src = qg + (size_t)min(pm_ld * 16 + rl, n - 1) * rsk;
 #pragma unroll
-        for (int kb = 0; kb < NKD; kb += X::GRP) X::ld_grp(src + X::doff(kb, g), &qf[kb]);
+        for (int kb = 0; kb < NKD; kb += X::GRP) X::ld_grp(src + X::doff(kb, g), &dst[kb]);
     };
 
     int item = blockIdx.x;
     if (!valid(item)) return;
     Item cur = decode(item);
     load_kg(cur);
-    load_q(cur);
+    load_q(cur, qf);
     if (wave > 0) touch_v(cur);
     for (;;) {
     const int c = cur.c, h = cur.h, b = cur.b;
@@ -327,6 +331,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const Item nxt = decode(more ? next : item);
 
     // ---- phase 1: K rows and K^T into LDS; gates -----------------------------------------------
+    // The item's prefetched registers are opaque until here, so that nothing derived from them
+    // is computed (and waited for) right after their loads were issued, an item earlier.
+#pragma unroll
+    for (int i = 0; i < PK; ++i) reg_fence(kr[i]);
     // rows to Ks; the transpose takes each thread's PK consecutive tokens of a column as one
     // contiguous run per column
     if (tid * PK < C * VK) {
@@ -392,9 +400,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
 #pragma unroll
     for (int i = 0; i < NVL; ++i) vsink ^= vl[i];
-    if (more) load_kg(nxt);   // registers consumed above; the next item's rows are in flight from here
 #pragma unroll
     for (int kb = 0; kb < NKD; ++kb) qf[kb] = X::keep_if(qf[kb], pm_ld * 16 + rl < n);
+    // every register loaded for this item is taken before the next item's loads are issued:
+    // the count of outstanding loads drains in issue order, so a wait for one of them placed
+    // after those loads would wait for them too
+#pragma unroll
+    for (int kb = 0; kb < NKD; ++kb) reg_fence(qf[kb]);
+    reg_fence(vsink);
+    asm volatile("" ::: "memory");
+    if (more) load_kg(nxt);   // registers consumed above; the next item's rows are in flight from here
     lds_barrier();   // (B1)
     if constexpr (NORM) {
         // 1 / |k_r| into this wave's copy (lane r sums row r's parts; rows past the chunk are
@@ -528,6 +543,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     };
 
     // ---- phase 2 -------------------------------------------------------------------------------
+    // bf16: the next item's Q rows and v lines, a whole item ahead of their use, in code common
+    // to all waves (see below for why not inside the branches)
+    if constexpr (QN) {
+        if (more) {
+            load_q(nxt, qn);
+            if (wave > 0) touch_v(nxt);
+        }
+    }
     if (wave == 0) {
         f32x4 Gd[NT], G1[NT / 2 > 0 ? NT / 2 : 1];
 #pragma unroll
@@ -536,7 +559,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int q = 0; q < NT / 2; ++q) G1[q] = kk_tile(2 * q + 1, 2 * q);
         p_row(0);
         store_rows(0);
-        if (more) load_q(nxt);
 #pragma unroll
         for (int d = 0; d < NT; ++d) mask_a(d, d, Gd[d]);
 #pragma unroll
@@ -598,10 +620,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             p_row(pm);
             store_rows(pm);
         }
-        if (more) {
-            load_q(nxt);
-            touch_v(nxt);
-        }
         if (NT == 4 && wave >= 2) {   // the 32x32 off-diagonal block, one tile column per wave
             const int tn = wave - 2;
             const f32x4 Ga = kk_tile(2, tn), Gb = kk_tile(3, tn);
@@ -616,6 +634,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             if ((r4 >> 4) < (s >> 4) || r4 >= C)
                 *reinterpret_cast<float4*>(sRT + s * LDR + r4) = make_float4(0.f, 0.f, 0.f, 0.f);
         }
+    }
+    // fp32: the next item's Q rows (and v lines) are loaded here, after the branches of phase 2
+    // rather than inside them: a register loaded in one branch and reused in the other would
+    // otherwise be waited for in both, and the branch of wave 0 would wait for the next item's
+    // K rows.
+    if (!QN && more) {
+        load_q(nxt, qf);
+        if (wave > 0) touch_v(nxt);
     }
     norm_gates();
     lds_barrier();   // (B2)
@@ -743,6 +769,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
     }
     if (!more) break;
+    if constexpr (QN) {
+#pragma unroll
+        for (int kb = 0; kb < NKD; ++kb) qf[kb] = qn[kb];
+    }
     lds_barrier();   // this item's LDS reads are done before the next item overwrites it
     item = next;
     cur = nxt;
