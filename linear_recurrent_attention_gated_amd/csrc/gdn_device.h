@@ -198,6 +198,24 @@ __device__ __forceinline__ float dpp_f(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (lane l gets x_0 + ... + x_l), on the VALU:
+// shifts by 1, 2, 4 and 8 lanes inside each row of 16 (DPP row_shr; a lane without a source
+// adds 0), then the last lane of rows 0 and 2 added into rows 1 and 3 (row_bcast:15) and the
+// last lane of row 1 into rows 2 and 3 (row_bcast:31).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, false));
+}
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x += dpp_or_zero<0x111, 0xf>(x);   // row_shr:1
+    x += dpp_or_zero<0x112, 0xf>(x);   // row_shr:2
+    x += dpp_or_zero<0x114, 0xf>(x);   // row_shr:4
+    x += dpp_or_zero<0x118, 0xf>(x);   // row_shr:8
+    x += dpp_or_zero<0x142, 0xa>(x);   // row_bcast:15, rows 1 and 3
+    x += dpp_or_zero<0x143, 0xc>(x);   // row_bcast:31, rows 2 and 3
+    return x;
+}
+
 template <int L>
 __device__ __forceinline__ float group_sum(float x) {
     static_assert(L == 4 || L == 8 || L == 16 || L == 32, "group size");

@@ -375,15 +375,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
     }
     if (wave == 0) {
-        float x = lane < n ? graw : 0.f;   // running log-gate; constant past the end
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(x, off, 64);
-            if (lane >= off) x += y;
-        }
+        // running log-gate; constant past the end
+        const float x = wave_prefix_sum(lane < n ? graw : 0.f);
         const float bt = lane < n ? braw : 0.f;
         const float x2 = x * LOG2E;
-        const float gl2 = __shfl(x2, C - 1, 64);
+        const float gl2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x2), C - 1));
         if (lane < C) sg2[lane] = x2;
         if (lane < CP) {
             sbeta[lane] = bt;
