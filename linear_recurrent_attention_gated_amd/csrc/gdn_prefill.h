@@ -153,9 +153,10 @@ __device__ __forceinline__ void store_run(E* dst, const E (&v)[8], int np) {
 // Kernel 1: per-chunk, state-independent blocks; one work item per (batch, value head,
 // chunk), four waves.
 //
-//   phase 0  the item's global loads, issued while the previous item is computed: K rows into
-//            registers, each wave's Q row tile as MFMA fragments, g and beta, and one word of
-//            every 128-byte line of the chunk's v rows (see touch_v)
+//   phase 0  the item's global loads, issued while the previous item is computed: K rows, g
+//            and beta at the end of its phase 1; each wave's Q row tile as MFMA fragments and
+//            one word of every 128-byte line of the chunk's v rows (see touch_v) as its phase 2
+//            starts (fp32: ends)
 //   phase 1  K rows and K^T (token-contiguous) into LDS; wave 0 scans the gates
 //   phase 2  wave 0: Gram tiles of the diagonal blocks and of the first off-diagonal
 //            level, masked into A; unit-lower-triangular 16x16 diagonal inverses by
@@ -261,9 +262,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     constexpr int PK = (C * VK + kThreads - 1) / kThreads;
     // v: this kernel does not use it, but the scan reads it on its critical path in 32-byte
     // pieces per row and state slice.  One 4-byte read of each 128-byte line of the chunk's v
-    // rows here (by waves 1..3, after the next item's other loads) brings them into the
-    // last-level cache while they are off that path; the words read are folded into vsink,
-    // which only an impossible condition stores.
+    // rows here (by waves 1..3, after the next item's Q loads) brings them into the last-level
+    // cache while they are off that path; the words read are folded into vsink, which only an
+    // impossible condition stores.
     constexpr int LPR = (DV * (int)sizeof(E) + 127) / 128;   // lines per v row
     constexpr int NVL = (C * LPR + kThreads - 65) / (kThreads - 64);
     // this wave's P row tile: wave 0 takes row 0, wave w >= 1 row NT - w (if >= 1)
