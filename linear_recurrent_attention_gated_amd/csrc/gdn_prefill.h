@@ -679,50 +679,81 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // accumulator tile with columns = the operand's rows.  A operands come from rows of sRT.
     {
         // Z^T tile (s-tile u, dk-tile dt) = sum over tokens r of (beta_s R[r][s] e_r) K[r][d].
-        // The waves split Z's stored k-blocks: a group is the TPG s-tiles one k-block of Z holds.
-        constexpr int TPG = KPL == 8 ? 2 : 1;
-        constexpr int NG = (NT + TPG - 1) / TPG;
-        const int zg = wave % NG;
-        frag az[TPG][NKC];
-#pragma unroll
-        for (int i = 0; i < TPG; ++i) {
-            const int u = zg * TPG + i;
-            const float* row = sRT + (min(u, NT - 1) * 16 + rl) * LDR;   // (s-tiles past the chunk: unused)
-#pragma unroll
-            for (int kb = 0; kb < NKC; ++kb) {
-                az[i][kb] = X::zero();
-                if (u < NT && kb_lo(kb) + KSPAN > u * 16) {   // blocks wholly before s-tile u are zero
-                    float t[KPL];
-#pragma unroll
-                    for (int e = 0; e < KPL; ++e) t[e] = row[kb * KB + kq + e] * se[kb * KB + kq + e];
-                    az[i][kb] = X::ld_f(t);
-                }
-            }
-        }
         E* Zg = reinterpret_cast<E*>(p.Z) + (bh * N + c) * S::Z_PER_CHUNK;
-        for (int dt = wave / NG; dt < ND; dt += 4 / NG) {
-            // B operand: K^T rows (dk) over tokens -- from KsT (bf16) or a column of Ks (fp32)
-            auto kt = [&](int kb) {
-                if constexpr (TRK) return X::ld(KsT + (dt * 16 + rl) * LDT + kq + kb * KB);
-                else return X::ld(Ks + (kb * KB + kq) * LDK + dt * 16 + rl);
-            };
-            f32x4 acc[TPG];
+        if constexpr (KPL == 1 && NT == 4 && ND == 8) {
+            // fp32, 64-token chunks, dk = 128: s-tile u needs the k-blocks from 4u on (16 - 4u
+            // products per dk tile), so wave w takes s-tile w for dk tiles 0..3 and s-tile 3 - w
+            // for 4..7 (the same count for every wave), two dk tiles at a time as independent
+            // product chains
 #pragma unroll
-            for (int i = 0; i < TPG; ++i) acc[i] = zero4();
+            for (int half = 0; half < 2; ++half) {
+                const int u = half == 0 ? wave : NT - 1 - wave;
+                const float* row = sRT + (u * 16 + rl) * LDR;
+                frag a[NKC];
 #pragma unroll
-            for (int kb = 0; kb < NKC; ++kb) {
-                const frag bk = kt(kb);
+                for (int kb = 0; kb < NKC; ++kb) a[kb] = kb >= 4 * u ? row[kb * KB + kq] * se[kb * KB + kq] : 0.f;
 #pragma unroll
-                for (int i = 0; i < TPG; ++i) {
-                    const int u = zg * TPG + i;
-                    if (u < NT && kb_lo(kb) + KSPAN > u * 16) acc[i] = X::mma(az[i][kb], bk, acc[i]);
+                for (int d2 = 0; d2 < 4; d2 += 2) {
+                    const int dt = half * 4 + d2;
+                    f32x4 c0 = zero4(), c1 = zero4();
+#pragma unroll
+                    for (int kb = 0; kb < NKC; ++kb) {
+                        if (kb >= 4 * u) {
+                            const E* kc = Ks + (kb * KB + kq) * LDK + dt * 16 + rl;
+                            c0 = X::mma(a[kb], kc[0], c0);
+                            c1 = X::mma(a[kb], kc[16], c1);
+                        }
+                    }
+                    const frag f0[4] = {c0[0], c0[1], c0[2], c0[3]}, f1[4] = {c1[0], c1[1], c1[2], c1[3]};
+                    X::st_grp(Zg + (size_t)dt * NKC * 64 * KPL + X::foff(4 * u, lane), f0);
+                    X::st_grp(Zg + (size_t)(dt + 1) * NKC * 64 * KPL + X::foff(4 * u, lane), f1);
                 }
             }
-            if constexpr (KPL == 8) {
-                *reinterpret_cast<frag*>(Zg + ((size_t)(dt * NKC + zg) * 64 + lane) * KPL) = X::pack(acc[0], acc[TPG - 1]);
-            } else {   // fragments 4 zg .. 4 zg + 3: one lane group
-                const frag f[4] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3]};
-                X::st_grp(Zg + (size_t)dt * NKC * 64 * KPL + X::foff(4 * zg, lane), f);
+        } else {
+            // The waves split Z's stored k-blocks: a group is the TPG s-tiles one k-block of Z holds.
+            constexpr int TPG = KPL == 8 ? 2 : 1;
+            constexpr int NG = (NT + TPG - 1) / TPG;
+            const int zg = wave % NG;
+            frag az[TPG][NKC];
+#pragma unroll
+            for (int i = 0; i < TPG; ++i) {
+                const int u = zg * TPG + i;
+                const float* row = sRT + (min(u, NT - 1) * 16 + rl) * LDR;   // (s-tiles past the chunk: unused)
+#pragma unroll
+                for (int kb = 0; kb < NKC; ++kb) {
+                    az[i][kb] = X::zero();
+                    if (u < NT && kb_lo(kb) + KSPAN > u * 16) {   // blocks wholly before s-tile u are zero
+                        float t[KPL];
+#pragma unroll
+                        for (int e = 0; e < KPL; ++e) t[e] = row[kb * KB + kq + e] * se[kb * KB + kq + e];
+                        az[i][kb] = X::ld_f(t);
+                    }
+                }
+            }
+            for (int dt = wave / NG; dt < ND; dt += 4 / NG) {
+                // B operand: K^T rows (dk) over tokens -- from KsT (bf16) or a column of Ks (fp32)
+                auto kt = [&](int kb) {
+                    if constexpr (TRK) return X::ld(KsT + (dt * 16 + rl) * LDT + kq + kb * KB);
+                    else return X::ld(Ks + (kb * KB + kq) * LDK + dt * 16 + rl);
+                };
+                f32x4 acc[TPG];
+#pragma unroll
+                for (int i = 0; i < TPG; ++i) acc[i] = zero4();
+#pragma unroll
+                for (int kb = 0; kb < NKC; ++kb) {
+                    const frag bk = kt(kb);
+#pragma unroll
+                    for (int i = 0; i < TPG; ++i) {
+                        const int u = zg * TPG + i;
+                        if (u < NT && kb_lo(kb) + KSPAN > u * 16) acc[i] = X::mma(az[i][kb], bk, acc[i]);
+                    }
+                }
+                if constexpr (KPL == 8) {
+                    *reinterpret_cast<frag*>(Zg + ((size_t)(dt * NKC + zg) * 64 + lane) * KPL) = X::pack(acc[0], acc[TPG - 1]);
+                } else {   // fragments 4 zg .. 4 zg + 3: one lane group
+                    const frag f[4] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3]};
+                    X::st_grp(Zg + (size_t)dt * NKC * 64 * KPL + X::foff(4 * zg, lane), f);
+                }
             }
         }
 

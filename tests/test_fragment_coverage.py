@@ -56,14 +56,22 @@ def intra_stores(elem, C, dk, split=kept_split):
             for kb in range(S["NKD"]):
                 put("KF", m * S["NKD"] + kb, w)
                 put("QF", m * S["NKD"] + kb, w)
-        # phase 4: Z, k-block groups split over the waves, dk tiles strided
-        zg, dt0, dts = split(w, S["NG"])
-        for dt in range(dt0, S["ND"], dts):
-            if elem == "bf16":
-                put("Z", dt * S["NKC"] + zg, w)
-            else:
+        # phase 4: Z.  fp32 at 64-token chunks and dk = 128: wave w takes s-tile w for dk tiles
+        # 0..3 and s-tile 3 - w for 4..7; otherwise k-block groups split over the waves, dk tiles
+        # strided
+        if elem == "f32" and S["NT"] == 4 and S["ND"] == 8 and split is kept_split:
+            for dt in range(S["ND"]):
+                u = w if dt < 4 else 3 - w
                 for j in range(4):
-                    put("Z", dt * S["NKC"] + 4 * zg + j, w)
+                    put("Z", dt * S["NKC"] + 4 * u + j, w)
+        else:
+            zg, dt0, dts = split(w, S["NG"])
+            for dt in range(dt0, S["ND"], dts):
+                if elem == "bf16":
+                    put("Z", dt * S["NKC"] + zg, w)
+                else:
+                    for j in range(4):
+                        put("Z", dt * S["NKC"] + 4 * zg + j, w)
         # phase 4: P', fragments wholly above the diagonal are never stored
         if m is not None:
             if elem == "bf16":
