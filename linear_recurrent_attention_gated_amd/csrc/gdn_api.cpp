@@ -174,8 +174,8 @@ gdn_status prefill_stages(const void* q, const void* k, const void* v, const flo
     if (noalloc) {   // every argument has been validated: now (only) look up the array
         if (layout(B, chunk, Hk, Hv, dk, dv, chunk, dtype).total > GDN_NOALLOC_SCRATCH_BYTES)
             return GDN_ERR_WORKSPACE;
-        const gdn_status st = scratch_address(&workspace);
-        if (st != GDN_OK) return st;
+        const gdn_status sa = scratch_address(&workspace);
+        if (sa != GDN_OK) return sa;
         workspace_bytes = GDN_NOALLOC_SCRATCH_BYTES;
     }
     if (!workspace) return GDN_ERR_WORKSPACE;
