@@ -82,16 +82,17 @@ size_t gdn_prefill_workspace_bytes(int B, int T, int Hk, int Hv, int dk, int dv,
  *   o          [B, T, Hv, dv] dtype      (o_t = S_t q_t, the post-update state read with q_t)
  *   state_out  [B, Hv, dv, dk] float     (state after token T-1; may equal state_in, which
  *                                         is then updated in place)
- *   workspace  device buffer, 256-byte aligned; may be NULL only when T == 0.  With
- *              gdn_prefill_workspace_bytes(...) bytes the prompt runs in one pass.  A
- *              smaller workspace bounds the temporary memory instead: the prompt is run
- *              in consecutive segments of the longest whole number of chunks whose
- *              workspace fits, and the state is carried from one to the next through
- *              state_out ("Optimizing on-device inference for Apple Silicon", section
- *              "Bound temporary memory with prompt chunking": segmenting a prompt and
- *              carrying the recurrent state leaves the output unchanged).  The result
- *              equals the one-pass result bit for bit.  GDN_ERR_WORKSPACE if not even one
- *              chunk fits.
+ *   workspace  device buffer, 256-byte aligned; may be NULL only when T == 0.
+ *              gdn_prefill_workspace_bytes(...) bytes hold the whole prompt.  The prompt
+ *              runs in consecutive passes of whole chunks, of equal length, with the state
+ *              carried from one to the next through state_out ("Optimizing on-device
+ *              inference for Apple Silicon", section "Bound temporary memory with prompt
+ *              chunking": segmenting a prompt and carrying the recurrent state leaves the
+ *              output unchanged), when the workspace is smaller (it bounds the temporary
+ *              memory) or when one pass's workspace and v rows would exceed the last-level
+ *              cache (about 176 MB for bf16 operands, 300 MB for fp32; passes that stay in it
+ *              run faster).  The result equals the one-pass result bit for bit.
+ *              GDN_ERR_WORKSPACE if not even one chunk fits.
  * T == 0 copies state_in (or zeros) to state_out and touches nothing else.
  * Outputs must not overlap each other, the inputs or the workspace, except
  * state_out == state_in exactly. */

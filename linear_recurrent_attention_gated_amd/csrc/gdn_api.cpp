@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 
@@ -47,6 +48,17 @@ int sequential_max_tokens(int B, int Hv, int dk, int dv, gdn_dtype dtype) {
     const double waves = (double)B * Hv * dv * (dk / 8) / 64.0;
     if (waves > 1024.0) t1 *= std::pow(1024.0 / waves, dtype == GDN_BF16 ? 0.42 : 0.66);
     return t1 < 1.0 ? 1 : (int)t1;
+}
+
+// Last-level-cache budget of one blockwise prefill pass: its workspace plus its v rows (what the
+// scan reads after the intra-chunk kernel has written or touched it).  MI355X has 256 MB of
+// last-level cache; measured there (16/32 heads, d = 128, cold): bf16 prompts of up to 6,144
+// tokens (~176 MB) run fastest in one pass, longer ones in equal passes of at most that many
+// (8K: 195 against 252 us in one pass; 128K: 2.9 against 3.5 ms).  fp32 passes lose less to
+// cache misses (their scan is slower per chunk): one pass stays best up to ~4,096 tokens
+// (226 MB), two passes win from ~6,144.
+size_t pass_cache_budget(gdn_dtype dtype) {
+    return dtype == GDN_BF16 ? ((size_t)176 << 20) : ((size_t)300 << 20);
 }
 
 // Workspace regions of the blockwise prefill (see gdn_prefill.h).
@@ -180,20 +192,40 @@ gdn_status prefill_stages(const void* q, const void* k, const void* v, const flo
     }
     if (!workspace) return GDN_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
-    // Tokens per pass: the whole prompt when the workspace holds it, otherwise (full prefill
-    // only) the longest whole number of chunks whose workspace fits; the passes then carry
-    // the state through state_out.
+    // Tokens per pass.  The stages alone need the one-pass workspace.  The full prefill runs the
+    // prompt in passes of whole chunks, carrying the state through state_out, when the workspace
+    // does not hold it in one, or when one pass would not keep its working set in the last-level
+    // cache (pass_cache_budget); the passes are then of equal length.
     int seg = T;
-    if (layout(B, T, Hk, Hv, dk, dv, chunk, dtype).total > workspace_bytes) {
-        if (stages != 3) return GDN_ERR_WORKSPACE;
-        int lo = 0, hi = (T + chunk - 1) / chunk;   // chunks per pass: lo fits, hi does not
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) / 2;
-            if (layout(B, mid * chunk, Hk, Hv, dk, dv, chunk, dtype).total <= workspace_bytes) lo = mid;
-            else hi = mid;
+    const int nchunks = (T + chunk - 1) / chunk;
+    if (stages != 3) {
+        if (layout(B, T, Hk, Hv, dk, dv, chunk, dtype).total > workspace_bytes) return GDN_ERR_WORKSPACE;
+    } else {
+        const size_t budget = pass_cache_budget(dtype);
+        // longest pass (in chunks) that satisfies pred, at most the whole prompt; 0 if none does
+        auto longest = [&](auto pred) {
+            if (pred(nchunks)) return nchunks;
+            int lo = 0, hi = nchunks;   // pred(lo) holds (or lo = 0), pred(hi) does not
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) / 2;
+                if (pred(mid)) lo = mid;
+                else hi = mid;
+            }
+            return lo;
+        };
+        const int ws_max = longest([&](int n) {
+            return layout(B, n * chunk, Hk, Hv, dk, dv, chunk, dtype).total <= workspace_bytes;
+        });
+        if (ws_max == 0) return GDN_ERR_WORKSPACE;
+        const int cache_max = std::max(1, longest([&](int n) {
+            return layout(B, n * chunk, Hk, Hv, dk, dv, chunk, dtype).total +
+                       (size_t)B * n * chunk * Hv * dv * es <= budget;
+        }));
+        const int cap = std::min(ws_max, cache_max);
+        if (cap < nchunks) {
+            const int npass = (nchunks + cap - 1) / cap;
+            seg = (nchunks + npass - 1) / npass * chunk;
         }
-        if (lo == 0) return GDN_ERR_WORKSPACE;
-        seg = lo * chunk;
     }
 
     for (int t0 = 0; t0 < T; t0 += seg) {

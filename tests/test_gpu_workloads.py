@@ -280,6 +280,26 @@ def test_prepare_then_scan_equals_one_call(dt):
     assert nrel(np32(oe), o_ref) < TOL_O and nrel(se.cpu().numpy(), s_ref) < TOL_S
 
 
+@pytest.mark.parametrize("dt,T", [(torch.bfloat16, 8292), (torch.float32, 6200)])
+def test_cache_sized_passes_equal_one_pass(dt, T):
+    # at 16/32 heads and d = 128 these prompts exceed one pass's last-level-cache budget, so
+    # gdn_prefill runs them in equal passes even with the one-pass workspace; the two stages
+    # called separately always make one pass: the results must be bitwise equal
+    d = to_dev(make_inputs(1, T, 16, 32, 128, 128, seed=27, state_std=0.1, dtype=dt))
+    nbytes = gdn.gdn_prefill_workspace_bytes(1, T, 16, 32, 128, 128, 64, dt)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    o1, o2 = torch.empty_like(d["v"]), torch.empty_like(d["v"])
+    s1 = torch.empty((1, 32, 128, 128), dtype=torch.float32, device="cuda")
+    s2 = torch.empty_like(s1)
+    say("cache-sized passes", dt, T)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"])
+    gdn.gdn_prefill(*args, o1, s1, 64, ws)
+    gdn.gdn_prefill_prepare(*args, o2, s2, 64, ws)
+    gdn.gdn_prefill_scan(*args, o2, s2, 64, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
 def test_long_128k_bounded_workspace(c4):
     # the 131072-token prompt with a 256 MiB workspace (the one-pass workspace is 2.5-5 GiB)
     dt, d, o_full, s_full = c4
