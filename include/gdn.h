@@ -90,7 +90,7 @@ size_t gdn_prefill_workspace_bytes(int B, int T, int Hk, int Hv, int dk, int dv,
  *              chunking": segmenting a prompt and carrying the recurrent state leaves the
  *              output unchanged), when the workspace is smaller (it bounds the temporary
  *              memory) or when one pass's workspace and v rows would exceed the last-level
- *              cache (about 176 MB for bf16 operands, 300 MB for fp32; passes that stay in it
+ *              cache (about 176 MB for bf16 operands, 600 MB for fp32; passes that stay in it
  *              run faster).  The result equals the one-pass result bit for bit.
  *              GDN_ERR_WORKSPACE if not even one chunk fits.
  * T == 0 copies state_in (or zeros) to state_out and touches nothing else.

@@ -54,11 +54,12 @@ int sequential_max_tokens(int B, int Hv, int dk, int dv, gdn_dtype dtype) {
 // scan reads after the intra-chunk kernel has written or touched it).  MI355X has 256 MB of
 // last-level cache; measured there (16/32 heads, d = 128, cold): bf16 prompts of up to 6,144
 // tokens (~176 MB) run fastest in one pass, longer ones in equal passes of at most that many
-// (8K: 195 against 252 us in one pass; 128K: 2.9 against 3.5 ms).  fp32 passes lose less to
-// cache misses (their scan is slower per chunk): one pass stays best up to ~4,096 tokens
-// (226 MB), two passes win from ~6,144.
+// (8K: 195 against 252 us in one pass; 128K: 2.9 against 3.5 ms; batch 2 at 4K: 217 against
+// 259 us).  fp32 passes lose less to cache misses (their scan is slower per chunk) and more to
+// each pass's fixed cost: 4-16K-token passes are 5-14% faster than one pass at 16-32K tokens,
+// but two passes of 2K tokens at batch 2 are 8% slower than one, so its budget is larger.
 size_t pass_cache_budget(gdn_dtype dtype) {
-    return dtype == GDN_BF16 ? ((size_t)176 << 20) : ((size_t)300 << 20);
+    return dtype == GDN_BF16 ? ((size_t)176 << 20) : ((size_t)600 << 20);
 }
 
 // Workspace regions of the blockwise prefill (see gdn_prefill.h).

@@ -280,7 +280,7 @@ def test_prepare_then_scan_equals_one_call(dt):
     assert nrel(np32(oe), o_ref) < TOL_O and nrel(se.cpu().numpy(), s_ref) < TOL_S
 
 
-@pytest.mark.parametrize("dt,T", [(torch.bfloat16, 8292), (torch.float32, 6200)])
+@pytest.mark.parametrize("dt,T", [(torch.bfloat16, 8292), (torch.float32, 12100)])
 def test_cache_sized_passes_equal_one_pass(dt, T):
     # at 16/32 heads and d = 128 these prompts exceed one pass's last-level-cache budget, so
     # gdn_prefill runs them in equal passes even with the one-pass workspace; the two stages
