@@ -141,8 +141,8 @@ gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const flo
                           unsigned flags);
 
 /* Longest prompt for which GDN_PATH_AUTO picks the sequential form at these sizes: the
- * crossover of the two forms measured on MI355X, by operand type and head size (bf16: 24, 27,
- * 45 tokens at dk = dv = 32, 64, 128; fp32: 55, 84, 119), lowered when batch x value heads x
+ * crossover of the two forms measured on MI355X, by operand type and head size (bf16: 43, 42,
+ * 42 tokens at dk = dv = 32, 64, 128; fp32: 89, 96, 110), lowered when batch x value heads x
  * rows exceed what the sequential form runs in one wave per SIMD.  0 for unsupported sizes. */
 int gdn_prefill_sequential_max_tokens(int B, int Hk, int Hv, int dk, int dv, gdn_dtype dtype);
 

@@ -32,20 +32,21 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // Longest prompt for which GDN_PATH_AUTO takes the token-sequential path: the crossover of the
 // two prefill forms measured on MI355X (cold calls, chunk 64), where their times cross.
 //   dk = dv:        32     64    128
-//   bf16 operands:  24     27     45      (the same at 4 and 32 value heads, batch 1)
-//   fp32 operands:  55     84    119
-// The token-sequential form holds a state row on dk / 8 lanes; up to 1,024 waves (one per
-// SIMD) its time per token does not depend on the rows, and the crossover does not either.
-// Above that its time grows with the rows while the blockwise form's short-prompt time barely
-// does: at batch 4, 32 value heads, d = 128 (4,096 waves) the crossings were 25 (bf16) and 48
-// (fp32), a power law in the waves with exponents 0.42 and 0.66.  Between the tabulated
+//   bf16 operands:  43     42     42      (the same at 4 and 32 value heads, batch 1)
+//   fp32 operands:  89     96    110
+// The token-sequential form holds a state row on 16 lanes; up to 1,024 waves (one per SIMD)
+// its time per token does not depend on the rows, and the crossover does not either.  Above
+// that its time grows with the rows while the blockwise form's short-prompt time barely does:
+// at batch 4, 32 value heads, d = 128 (4,096 waves) the crossings were 24 (bf16) and 46
+// (fp32), a power law in the waves with exponents 0.42 and 0.66 (bf16 at d = 64, 2,048 waves:
+// 28 measured, 31 by the law).  Between the tabulated
 // dk * dv the crossover is interpolated in log2(dk * dv).
 int sequential_max_tokens(int B, int Hv, int dk, int dv, gdn_dtype dtype) {
-    static const double kBf16[3] = {24.0, 27.0, 45.0}, kF32[3] = {55.0, 84.0, 119.0};
+    static const double kBf16[3] = {43.0, 42.0, 42.0}, kF32[3] = {89.0, 96.0, 110.0};
     const double* t = dtype == GDN_BF16 ? kBf16 : kF32;
     const double x = std::log2((double)dk * dv);   // 10 .. 14
     double t1 = x <= 12.0 ? t[0] + (t[1] - t[0]) * (x - 10.0) / 2.0 : t[1] + (t[2] - t[1]) * (x - 12.0) / 2.0;
-    const double waves = (double)B * Hv * dv * (dk / 8) / 64.0;
+    const double waves = (double)B * Hv * dv * 16 / 64.0;
     if (waves > 1024.0) t1 *= std::pow(1024.0 / waves, dtype == GDN_BF16 ? 0.42 : 0.66);
     return t1 < 1.0 ? 1 : (int)t1;
 }

@@ -17,8 +17,8 @@
 //   S_i <- a_t S_i + delta k_t
 //   o_t[i] = S_i(new) . q_t = a_t s_q + delta (k_t . q_t)
 //
-// Mapping: a row of dk fp32 values is split over L = dk / 8 consecutive lanes, 8 values per
-// lane, so the reductions are log2(L) DPP steps on the VALU.  A workgroup holds up to 256 / L
+// Mapping: a row of dk fp32 values is split over L = 16 consecutive lanes, dk / 16 values per
+// lane, so the reductions are four DPP steps on the VALU.  A workgroup holds up to 256 / L
 // rows of one value head; each lane keeps its 8 state values in registers for all T tokens.
 // The token inputs (its 8 elements of q_t and k_t, v_t[i], g_t, beta_t) are independent of
 // the state, so they are loaded U tokens ahead into a second register set while the current
@@ -32,47 +32,71 @@
 
 namespace gdn {
 
-// 8 consecutive elements of q or k, loaded as 16-byte vectors
-template <typename E> struct Vec8;
-template <> struct Vec8<bf16_t> {
-    uint4 u;
-    __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
-    __device__ __forceinline__ void to_f(float (&f)[8]) const {
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+// N (8, 4 or 2) consecutive elements of q or k, loaded as one or two vectors
+template <typename E, int N> struct VecN;
+template <int N> struct VecN<bf16_t, N> {
+    static_assert(N == 8 || N == 4 || N == 2, "8, 4 or 2 elements");
+    uint32_t w[N / 2];
+    __device__ __forceinline__ void load(const bf16_t* p) {
+        if constexpr (N == 8) {
+            const uint4 u = *reinterpret_cast<const uint4*>(p);
+            w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+        } else if constexpr (N == 4) {
+            const uint2 u = *reinterpret_cast<const uint2*>(p);
+            w[0] = u.x; w[1] = u.y;
+        } else {
+            w[0] = *reinterpret_cast<const uint32_t*>(p);
+        }
+    }
+    __device__ __forceinline__ void to_f(float (&f)[N]) const {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < N / 2; ++i) {
             f[2 * i] = __uint_as_float(w[i] << 16);
             f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
         }
     }
 };
-template <> struct Vec8<float> {
-    float4 a, b;
+template <int N> struct VecN<float, N> {
+    static_assert(N == 8 || N == 4 || N == 2, "8, 4 or 2 elements");
+    float f_[N];
     __device__ __forceinline__ void load(const float* p) {
-        a = *reinterpret_cast<const float4*>(p);
-        b = *reinterpret_cast<const float4*>(p + 4);
+        if constexpr (N == 2) {
+            const float2 a = *reinterpret_cast<const float2*>(p);
+            f_[0] = a.x; f_[1] = a.y;
+        } else {
+#pragma unroll
+            for (int i = 0; i < N / 4; ++i) {
+                const float4 a = *reinterpret_cast<const float4*>(p + 4 * i);
+                f_[4 * i] = a.x; f_[4 * i + 1] = a.y; f_[4 * i + 2] = a.z; f_[4 * i + 3] = a.w;
+            }
+        }
     }
-    __device__ __forceinline__ void to_f(float (&f)[8]) const {
-        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    __device__ __forceinline__ void to_f(float (&f)[N]) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) f[i] = f_[i];
     }
 };
 
+// A state row is split over L = 16 lanes (one DPP row, so its reductions need no cross-row
+// step): dk / 16 values per lane.  Measured at 16/32 heads: at d = 128, rows over 32 lanes (4
+// values each) ran 1.5x slower; at d = 64 and 32, rows over 8 and 4 lanes (8 values each)
+// left most SIMDs without a wave and ran 1.8-1.9x slower.
 template <int DK, int DV>
 struct SeqShape {
-    static constexpr int EPL = 8;                                  // state values per lane
-    static constexpr int L = DK / EPL;                             // lanes per row
+    static constexpr int L = 16;                                   // lanes per row
+    static constexpr int EPL = DK / L;                             // state values per lane
     static constexpr int NTH = DV * L < 256 ? DV * L : 256;       // threads per workgroup
     static constexpr int RPB = NTH / L;                            // rows per workgroup
     static constexpr int NBLK = DV / RPB;                          // workgroups per head
-    static_assert(L >= 4 && L <= 16 && NBLK * RPB == DV, "sequential tiling");
+    static_assert((EPL == 2 || EPL == 4 || EPL == 8) && NBLK * RPB == DV, "sequential tiling");
 };
 
-// a . b over 8 values, as two interleaved FMA chains
-__device__ __forceinline__ float dot8(const float (&a)[8], const float (&b)[8]) {
+// a . b over N values, as two interleaved FMA chains
+template <int N>
+__device__ __forceinline__ float dotn(const float (&a)[N], const float (&b)[N]) {
     float x = a[0] * b[0], y = a[1] * b[1];
 #pragma unroll
-    for (int e = 2; e < 8; e += 2) {
+    for (int e = 2; e < N; e += 2) {
         x = fmaf(a[e], b[e], x);
         y = fmaf(a[e + 1], b[e + 1], y);
     }
@@ -111,7 +135,7 @@ __global__ __launch_bounds__(256) void sequential_kernel(PrefillParams p) {
     const int koff = sub * EPL;
 
     struct Block {
-        Vec8<E> k[U], q[U];
+        VecN<E, EPL> k[U], q[U];
         E v[U];
         float g[U], beta[U];
     };
@@ -131,15 +155,12 @@ __global__ __launch_bounds__(256) void sequential_kernel(PrefillParams p) {
     float st[EPL];
     {
         const size_t srow = (((size_t)b * p.Hv + h) * DV + i) * DK + sub * EPL;
-        if (p.state_in) {
-            const float4 a = *reinterpret_cast<const float4*>(p.state_in + srow);
-            const float4 c = *reinterpret_cast<const float4*>(p.state_in + srow + 4);
-            st[0] = a.x; st[1] = a.y; st[2] = a.z; st[3] = a.w;
-            st[4] = c.x; st[5] = c.y; st[6] = c.z; st[7] = c.w;
-        } else {
+        VecN<float, EPL> s0;
+        if (p.state_in) s0.load(p.state_in + srow);
+        else
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) st[e] = 0.f;
-        }
+            for (int e = 0; e < EPL; ++e) s0.f_[e] = 0.f;
+        s0.to_f(st);
     }
 
     // U tokens from a loaded block; GUARD: tokens past T are skipped (uniform branches)
@@ -153,14 +174,14 @@ __global__ __launch_bounds__(256) void sequential_kernel(PrefillParams p) {
             x.k[u].to_f(kk);
             x.q[u].to_f(qq);
             if constexpr (NORM) {   // the L lanes of a row hold the whole vector between them
-                float ssk = dot8(kk, kk), ssq = dot8(qq, qq);
+                float ssk = dotn(kk, kk), ssq = dotn(qq, qq);
                 group_sum2<L>(ssk, ssq);
                 const float ik = rsqrtf(ssk + kNormEps), iq = rsqrtf(ssq + kNormEps);
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) { kk[e] *= ik; qq[e] *= iq; }
             }
             const float a = __builtin_amdgcn_exp2f(x.g[u] * LOG2E);
-            float kq = dot8(kk, qq), sk = dot8(st, kk), sq = dot8(st, qq);
+            float kq = dotn(kk, qq), sk = dotn(st, kk), sq = dotn(st, qq);
             group_sum3<L>(sk, sq, kq);
             const float delta = x.beta[u] * (X::to_f(x.v[u]) - a * sk);
 #pragma unroll
@@ -190,8 +211,13 @@ __global__ __launch_bounds__(256) void sequential_kernel(PrefillParams p) {
     }
 
     const size_t srow = (((size_t)b * p.Hv + h) * DV + i) * DK + sub * EPL;
-    *reinterpret_cast<float4*>(p.state_out + srow) = make_float4(st[0], st[1], st[2], st[3]);
-    *reinterpret_cast<float4*>(p.state_out + srow + 4) = make_float4(st[4], st[5], st[6], st[7]);
+    if constexpr (EPL == 2) {
+        *reinterpret_cast<float2*>(p.state_out + srow) = make_float2(st[0], st[1]);
+    } else {
+#pragma unroll
+        for (int e4 = 0; e4 < EPL; e4 += 4)
+            *reinterpret_cast<float4*>(p.state_out + srow + e4) = make_float4(st[e4], st[e4 + 1], st[e4 + 2], st[e4 + 3]);
+    }
 }
 
 template <typename E, int DK, int DV>

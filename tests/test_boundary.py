@@ -143,12 +143,13 @@ def test_prefill_ex_validates_on_every_path(kw, code, flags):
 def test_sequential_crossover_follows_the_measured_table():
     f = gdn.gdn_prefill_sequential_max_tokens
     # batch 1 at 32 value heads: the measured crossovers (bf16, fp32) x (d = 32, 64, 128)
-    assert [f(1, 16, 32, d, d, 0) for d in (32, 64, 128)] == [24, 27, 45]
-    assert [f(1, 16, 32, d, d, 1) for d in (32, 64, 128)] == [55, 84, 119]
-    assert f(1, 2, 4, 128, 128, 0) == 45                   # fewer heads: unchanged
-    assert 20 <= f(4, 16, 32, 128, 128, 0) <= 30           # batch 4 measured 25
-    assert 43 <= f(4, 16, 32, 128, 128, 1) <= 53           # batch 4 measured 48
-    assert 24 < f(1, 16, 32, 64, 128, 0) < 45              # between the tabulated sizes
+    assert [f(1, 16, 32, d, d, 0) for d in (32, 64, 128)] == [43, 42, 42]
+    assert [f(1, 16, 32, d, d, 1) for d in (32, 64, 128)] == [89, 96, 110]
+    assert f(1, 2, 4, 128, 128, 0) == 42                   # fewer heads: unchanged
+    assert 19 <= f(4, 16, 32, 128, 128, 0) <= 29           # batch 4 measured 24
+    assert 41 <= f(4, 16, 32, 128, 128, 1) <= 51           # batch 4 measured 46
+    assert 25 <= f(4, 16, 32, 64, 64, 0) <= 33             # 2,048 waves, measured 28
+    assert 96 < f(1, 16, 32, 64, 128, 1) < 110             # between the tabulated sizes
     assert f(1000, 16, 32, 128, 128, 0) >= 1
     assert f(1, 16, 32, 96, 128, 0) == 0                   # unsupported size
 
