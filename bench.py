@@ -21,8 +21,9 @@ decode roofline), one B = 30 launch over states stored back to back, 30 B = 1 la
 the 30 launches captured in a HIP graph.  Secondary: the same prefill call alone right after
 a 1 GiB flush fill (one call between two events), the two kernels timed as the two stages
 (gdn_prefill_prepare, then gdn_prefill_scan) with an event between them, warm-cache stages,
-the fused-normalisation and all-fp32 calls, and a plain device copy as the achievable-
-bandwidth reference.  The CPU oracle runs on the host on the same prefill workload,
+the fused-normalisation and all-fp32 calls, the 131072-token long-memory prompt (gdn_prefill,
+which runs it in passes sized to the last-level cache, against one pass over the whole prompt),
+and a plain device copy as the achievable-bandwidth reference.  The CPU oracle runs on the host on the same prefill workload,
 alternating with cold GPU calls (its output doubles as a parity check of the GPU output).
 """
 import argparse
@@ -456,8 +457,8 @@ def main():
     import torch
 
     from linear_recurrent_attention_gated_amd import gdn
-    from linear_recurrent_attention_gated_amd.inputs import (PREFILL_4K, decode_inputs,
-                                                             workload_inputs)
+    from linear_recurrent_attention_gated_amd.inputs import (LONG_128K, PREFILL_4K, decode_inputs,
+                                                             make_inputs, workload_inputs)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -652,7 +653,6 @@ def main():
                 ts.append(a.elapsed_time(b2) * 1e3)
         return float(np.mean(ts))
 
-    from linear_recurrent_attention_gated_amd.inputs import make_inputs
     raw = make_inputs(B, T, Hk, Hv, dk, dv, w.seed, torch.bfloat16, unit_qk=False)
     rq, rk = raw["q"].to(dev), raw["k"].to(dev)
     o_v = torch.empty((B, T, Hv, dv), dtype=torch.bfloat16, device=dev)   # own outputs: set 0's
@@ -670,6 +670,29 @@ def main():
            B, T, Hk, Hv, dk, dv, C, gdn.GDN_F32, ws32.data_ptr(), ws32.numel(), sh)
     f32_us = cold_prefill_us(lib.gdn_prefill, a32, 10)
     del f32, o32, ws32, o_v, s_v
+
+    # -- the 128K long-memory prompt, cold: gdn_prefill (passes sized to the last-level cache)
+    # against one pass over the whole prompt (the two stages called separately).  Its inputs are
+    # drawn on the GPU (the same recipe as the oracle-checked CPU draw, another draw). --------
+    Lw = LONG_128K
+    lg = make_inputs(Lw.B, Lw.T, Lw.Hk, Lw.Hv, Lw.dk, Lw.dv, Lw.seed, torch.bfloat16, Lw.g_mean,
+                     Lw.beta_mean, device=dev)
+    lo = torch.empty((Lw.B, Lw.T, Lw.Hv, Lw.dv), dtype=torch.bfloat16, device=dev)
+    ls = torch.empty((Lw.B, Lw.Hv, Lw.dv, Lw.dk), dtype=torch.float32, device=dev)
+    lws_bytes = gdn.gdn_prefill_workspace_bytes(Lw.B, Lw.T, Lw.Hk, Lw.Hv, Lw.dk, Lw.dv, Lw.chunk,
+                                                torch.bfloat16)
+    lws = torch.empty(lws_bytes, dtype=torch.uint8, device=dev)
+    la = (lg["q"].data_ptr(), lg["k"].data_ptr(), lg["v"].data_ptr(), lg["g"].data_ptr(),
+          lg["beta"].data_ptr(), None, lo.data_ptr(), ls.data_ptr(), Lw.B, Lw.T, Lw.Hk, Lw.Hv,
+          Lw.dk, Lw.dv, Lw.chunk, gdn.GDN_BF16, lws.data_ptr(), lws_bytes, sh)
+
+    def one_pass(*a):
+        rc = lib.gdn_prefill_prepare(*a)
+        return rc if rc else lib.gdn_prefill_scan(*a)
+
+    long_passes_us = cold_prefill_us(lib.gdn_prefill, la, 3)
+    long_one_us = cold_prefill_us(one_pass, la, 3)
+    del lg, lo, ls, lws
 
     # -- achievable HBM bandwidth in the same run: a plain device-to-device copy of known
     # size, cold (it is also the reference point of the HBM byte counters) -----------------
@@ -741,6 +764,12 @@ def main():
             "warm_inter_chunk_us": round(float(tw_inter.mean()), 2),
             "qknorm_us": round(qknorm_us, 2),
             "f32_us": round(f32_us, 2),
+            "long_131072": {
+                "workload": LONG_128K.name + ", bf16, zero start state, cold single calls",
+                "us_cache_sized_passes": round(long_passes_us, 1),
+                "mtok_s_cache_sized_passes": round(LONG_128K.T / long_passes_us, 2),
+                "us_one_pass": round(long_one_us, 1),
+                "mtok_s_one_pass": round(LONG_128K.T / long_one_us, 2)},
             "mfma_tflops": round(pf_flops / (mean_pf * 1e-6) / 1e12, 2),
             "mfma_frac": round(pf_flops / (mean_pf * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         },

@@ -60,27 +60,30 @@ def _unit(x: torch.Tensor) -> torch.Tensor:
 
 
 def make_inputs(B, T, Hk, Hv, dk, dv, seed, dtype=torch.bfloat16, g_mean=0.0, beta_mean=0.0,
-                state_std: Optional[float] = None, unit_qk: bool = True):
-    """Returns dict(q, k, v, g, beta, state) of CPU tensors.
+                state_std: Optional[float] = None, unit_qk: bool = True, device="cpu"):
+    """Returns dict(q, k, v, g, beta, state) of tensors on ``device`` (CPU by default; the
+    values depend on the device's generator, so a draw on another device is a different draw
+    of the same recipe).
 
     q, k [B,T,Hk,dk] and v [B,T,Hv,dv] in ``dtype``; g, beta [B,T,Hv] fp32;
     state [B,Hv,dv,dk] fp32 or None.  unit_qk=False leaves q and k unnormalised, as raw
     projections: N(0, 1) entries times a per-token length factor exp(N(0, 0.5^2)), drawn
     after everything else so the other tensors equal the unit_qk=True draw."""
-    gen = torch.Generator("cpu").manual_seed(int(seed))
-    qr = torch.randn(B, T, Hk, dk, generator=gen)
-    kr = torch.randn(B, T, Hk, dk, generator=gen)
-    v = torch.randn(B, T, Hv, dv, generator=gen).to(dtype)
-    g = -F.softplus(torch.randn(B, T, Hv, generator=gen) + g_mean)
-    beta = torch.sigmoid(torch.randn(B, T, Hv, generator=gen) + beta_mean)
+    gen = torch.Generator(device).manual_seed(int(seed))
+    rn = lambda *shape: torch.randn(*shape, generator=gen, device=device)  # noqa: E731
+    qr = rn(B, T, Hk, dk)
+    kr = rn(B, T, Hk, dk)
+    v = rn(B, T, Hv, dv).to(dtype)
+    g = -F.softplus(rn(B, T, Hv) + g_mean)
+    beta = torch.sigmoid(rn(B, T, Hv) + beta_mean)
     state = None
     if state_std is not None:
-        state = torch.randn(B, Hv, dv, dk, generator=gen) * state_std
+        state = rn(B, Hv, dv, dk) * state_std
     if unit_qk:
         q, k = _unit(qr).to(dtype), _unit(kr).to(dtype)
     else:
-        q = (qr * torch.exp(0.5 * torch.randn(B, T, Hk, 1, generator=gen))).to(dtype)
-        k = (kr * torch.exp(0.5 * torch.randn(B, T, Hk, 1, generator=gen))).to(dtype)
+        q = (qr * torch.exp(0.5 * rn(B, T, Hk, 1))).to(dtype)
+        k = (kr * torch.exp(0.5 * rn(B, T, Hk, 1))).to(dtype)
     return dict(q=q, k=k, v=v, g=g.contiguous(), beta=beta.contiguous(), state=state)
 
 
