@@ -129,9 +129,9 @@ def summarize_counters(fetch_dir, write_dir):
     w_scale = write.get("copy", 0) / COPY_CALIBRATION_BYTES
     lines = ["# HBM bytes per dispatch (rocprofv3 FETCH_SIZE / WRITE_SIZE counters), made by:",
              "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o fetch -- "
-             "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration" % fetch_dir,
+             "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration --skip-long" % fetch_dir,
              "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o write -- "
-             "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration" % write_dir,
+             "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration --skip-long" % write_dir,
              "#   python bench.py --summarize-counters %s %s" % (fetch_dir, write_dir),
              "# Raw counter bytes are divided by the factor the same counter reads for a plain",
              "# device-to-device copy of %d bytes (read and written once)." % COPY_CALIBRATION_BYTES,
@@ -167,6 +167,9 @@ def parse():
                     help="accepted for older command lines: the plain device-to-device copy of "
                          "known size (the reference point for the HBM byte counters and the "
                          "achievable-bandwidth figure) now runs in every measurement")
+    ap.add_argument("--skip-long", action="store_true",
+                    help="leave out the 131072-token secondary (the HBM counter runs do: its launches "
+                         "are the same kernels and would enter the per-launch averages)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script "
                          "with --copy-calibration into profiles/hbm_traffic.txt, then exit")
@@ -365,7 +368,8 @@ def summarize_trace(trace_dir, warmup, steps, bench_out=None):
            "launches, 3 x %d B=30 decode launches, 3 x %d x 30 B=1 decode launches, %d single cold" % (K, K, K + 1),
            "prefill calls (flush fill first), %d cold split-stage calls, 3 x %d replays of a HIP graph" % (K + 2, K),
            "of the 30 B=1 launches, %d warm split-stage calls, 11 cold fused-normalisation calls (their" % (K + 2),
-           "scan is the bf16 inter kernel), 11 cold all-fp32 calls (`float` instances) and a 512 MiB",
+           "scan is the bf16 inter kernel), 11 cold all-fp32 calls (`float` instances), 4 + 4 cold",
+           "calls of the 131072-token prompt (in cache-sized passes, then in one pass) and a 512 MiB",
            "device copy.  Averages over all launches of a kernel therefore mix these phases; the",
            "phase tables below split them.",
            "",
@@ -671,28 +675,30 @@ def main():
     f32_us = cold_prefill_us(lib.gdn_prefill, a32, 10)
     del f32, o32, ws32, o_v, s_v
 
-    # -- the 128K long-memory prompt, cold: gdn_prefill (passes sized to the last-level cache)
-    # against one pass over the whole prompt (the two stages called separately).  Its inputs are
-    # drawn on the GPU (the same recipe as the oracle-checked CPU draw, another draw). --------
-    Lw = LONG_128K
-    lg = make_inputs(Lw.B, Lw.T, Lw.Hk, Lw.Hv, Lw.dk, Lw.dv, Lw.seed, torch.bfloat16, Lw.g_mean,
-                     Lw.beta_mean, device=dev)
-    lo = torch.empty((Lw.B, Lw.T, Lw.Hv, Lw.dv), dtype=torch.bfloat16, device=dev)
-    ls = torch.empty((Lw.B, Lw.Hv, Lw.dv, Lw.dk), dtype=torch.float32, device=dev)
-    lws_bytes = gdn.gdn_prefill_workspace_bytes(Lw.B, Lw.T, Lw.Hk, Lw.Hv, Lw.dk, Lw.dv, Lw.chunk,
-                                                torch.bfloat16)
-    lws = torch.empty(lws_bytes, dtype=torch.uint8, device=dev)
-    la = (lg["q"].data_ptr(), lg["k"].data_ptr(), lg["v"].data_ptr(), lg["g"].data_ptr(),
-          lg["beta"].data_ptr(), None, lo.data_ptr(), ls.data_ptr(), Lw.B, Lw.T, Lw.Hk, Lw.Hv,
-          Lw.dk, Lw.dv, Lw.chunk, gdn.GDN_BF16, lws.data_ptr(), lws_bytes, sh)
+    long_passes_us = long_one_us = None
+    if not args.skip_long:
+        # -- the 128K long-memory prompt, cold: gdn_prefill (passes sized to the last-level cache)
+        # against one pass over the whole prompt (the two stages called separately).  Its inputs are
+        # drawn on the GPU (the same recipe as the oracle-checked CPU draw, another draw). --------
+        Lw = LONG_128K
+        lg = make_inputs(Lw.B, Lw.T, Lw.Hk, Lw.Hv, Lw.dk, Lw.dv, Lw.seed, torch.bfloat16, Lw.g_mean,
+                         Lw.beta_mean, device=dev)
+        lo = torch.empty((Lw.B, Lw.T, Lw.Hv, Lw.dv), dtype=torch.bfloat16, device=dev)
+        ls = torch.empty((Lw.B, Lw.Hv, Lw.dv, Lw.dk), dtype=torch.float32, device=dev)
+        lws_bytes = gdn.gdn_prefill_workspace_bytes(Lw.B, Lw.T, Lw.Hk, Lw.Hv, Lw.dk, Lw.dv, Lw.chunk,
+                                                    torch.bfloat16)
+        lws = torch.empty(lws_bytes, dtype=torch.uint8, device=dev)
+        la = (lg["q"].data_ptr(), lg["k"].data_ptr(), lg["v"].data_ptr(), lg["g"].data_ptr(),
+              lg["beta"].data_ptr(), None, lo.data_ptr(), ls.data_ptr(), Lw.B, Lw.T, Lw.Hk, Lw.Hv,
+              Lw.dk, Lw.dv, Lw.chunk, gdn.GDN_BF16, lws.data_ptr(), lws_bytes, sh)
 
-    def one_pass(*a):
-        rc = lib.gdn_prefill_prepare(*a)
-        return rc if rc else lib.gdn_prefill_scan(*a)
+        def one_pass(*a):
+            rc = lib.gdn_prefill_prepare(*a)
+            return rc if rc else lib.gdn_prefill_scan(*a)
 
-    long_passes_us = cold_prefill_us(lib.gdn_prefill, la, 3)
-    long_one_us = cold_prefill_us(one_pass, la, 3)
-    del lg, lo, ls, lws
+        long_passes_us = cold_prefill_us(lib.gdn_prefill, la, 3)
+        long_one_us = cold_prefill_us(one_pass, la, 3)
+        del lg, lo, ls, lws
 
     # -- achievable HBM bandwidth in the same run: a plain device-to-device copy of known
     # size, cold (it is also the reference point of the HBM byte counters) -----------------
@@ -764,7 +770,7 @@ def main():
             "warm_inter_chunk_us": round(float(tw_inter.mean()), 2),
             "qknorm_us": round(qknorm_us, 2),
             "f32_us": round(f32_us, 2),
-            "long_131072": {
+            "long_131072": None if long_passes_us is None else {
                 "workload": LONG_128K.name + ", bf16, zero start state, cold single calls",
                 "us_cache_sized_passes": round(long_passes_us, 1),
                 "mtok_s_cache_sized_passes": round(LONG_128K.T / long_passes_us, 2),
