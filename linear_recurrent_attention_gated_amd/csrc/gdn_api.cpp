@@ -219,10 +219,13 @@ gdn_status prefill_stages(const void* q, const void* k, const void* v, const flo
             return layout(B, n * chunk, Hk, Hv, dk, dv, chunk, dtype).total <= workspace_bytes;
         });
         if (ws_max == 0) return GDN_ERR_WORKSPACE;
-        const int cache_max = std::max(1, longest([&](int n) {
+        // passes shorter than ~512 tokens would pay their fixed cost for little: when the
+        // budget holds fewer (many heads or batches), the cache is not a reason to split
+        int cache_max = longest([&](int n) {
             return layout(B, n * chunk, Hk, Hv, dk, dv, chunk, dtype).total +
                        (size_t)B * n * chunk * Hv * dv * es <= budget;
-        }));
+        });
+        if (cache_max * chunk < 512) cache_max = nchunks;
         const int cap = std::min(ws_max, cache_max);
         if (cap < nchunks) {
             const int npass = (nchunks + cap - 1) / cap;
