@@ -130,8 +130,9 @@ gdn_status gdn_prefill_qknorm(const void *q, const void *k, const void *v, const
  *     state row split over a few lanes, held in registers for all T tokens, reduced across
  *     lanes per token, written once at the end; one launch, fp32 throughout.  The workspace
  *     is not used (it may be NULL; when given it still takes part in the overlap checks).
- *   GDN_PATH_AUTO: the sequential form for T <= gdn_prefill_sequential_max_tokens(...),
- *     else the blockwise form.
+ *   GDN_PATH_AUTO: for T == 1 with a start state, the decode step (gdn_decode_step or its
+ *     _qknorm form: one read and one write of the state); otherwise the sequential form for
+ *     T <= gdn_prefill_sequential_max_tokens(...), else the blockwise form.
  * Arguments, aliasing rules and status codes as gdn_prefill; chunk is validated whatever
  * the path.  GDN_ERR_UNSUPPORTED for unknown flag bits or both path bits. */
 gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const float *g,

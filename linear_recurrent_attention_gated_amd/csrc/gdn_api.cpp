@@ -283,6 +283,15 @@ gdn_status gdn_prefill_ex(const void* q, const void* k, const void* v, const flo
         ((flags & GDN_PATH_SEQUENTIAL) && (flags & GDN_PATH_AUTO)))
         return GDN_ERR_UNSUPPORTED;
     bool seq = (flags & GDN_PATH_SEQUENTIAL) != 0;
+    if ((flags & GDN_PATH_AUTO) && T == 1 && state_in) {
+        // one token from a given state: the decode step, a single read and write of the state
+        // (its layouts are the prefill's at T = 1)
+        const gdn_status sc = shape_check(B, T, Hk, Hv, dk, dv, chunk, dtype, true);
+        if (sc != GDN_OK) return sc;
+        return (flags & GDN_QK_NORM)
+                   ? gdn_decode_step_qknorm(q, k, v, g, beta, state_in, state_out, o, B, Hk, Hv, dk, dv, dtype, stream)
+                   : gdn_decode_step(q, k, v, g, beta, state_in, state_out, o, B, Hk, Hv, dk, dv, dtype, stream);
+    }
     if (flags & GDN_PATH_AUTO) seq = T <= gdn_prefill_sequential_max_tokens(B, Hk, Hv, dk, dv, dtype);
     return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
                           dtype, workspace, workspace_bytes, stream, 3,

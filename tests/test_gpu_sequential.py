@@ -95,3 +95,29 @@ def test_auto_picks_by_length(qk_norm):
                              qk_norm=qk_norm, path=expect)
         torch.cuda.synchronize()
         assert torch.equal(oa, oe) and torch.equal(sa, se), (T, expect)
+
+
+@pytest.mark.parametrize("qk_norm", [False, True], ids=["plain", "qknorm"])
+def test_auto_one_token_is_the_decode_step(qk_norm):
+    # one token from a given state: the automatic choice is the decode step, bitwise equal to
+    # gdn_decode_step on the same (T = 1) tensors, and within the oracle's tolerances; without
+    # a start state it stays the sequential form
+    Hk, Hv, dk, dv = 2, 4, 128, 64
+    h = make_inputs(2, 1, Hk, Hv, dk, dv, seed=34, state_std=0.2, unit_qk=not qk_norm)
+    d = to_dev(h)
+    say("auto one token", qk_norm)
+    oa, sa = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], chunk=64,
+                         qk_norm=qk_norm, path="auto")
+    st = d["state"].clone()
+    od = gdn.decode_step(d["q"][:, 0].contiguous(), d["k"][:, 0].contiguous(),
+                         d["v"][:, 0].contiguous(), d["g"][:, 0].contiguous(),
+                         d["beta"][:, 0].contiguous(), st, qk_norm=qk_norm)
+    o0, s0 = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], None, chunk=64,
+                         qk_norm=qk_norm, path="auto")
+    o0s, s0s = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], None, chunk=64,
+                           qk_norm=qk_norm, path="sequential")
+    torch.cuda.synchronize()
+    assert torch.equal(oa[:, 0], od) and torch.equal(sa, st)
+    assert torch.equal(o0, o0s) and torch.equal(s0, s0s)
+    o_ref, s_ref = oracle_prefill(h, h["state"], qk_norm=qk_norm)
+    assert nrel(np32(oa), o_ref) < TOL_O and nrel(sa.cpu().numpy(), s_ref) < TOL_S
