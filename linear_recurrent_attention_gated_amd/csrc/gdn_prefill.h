@@ -1129,7 +1129,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
                 for (int kb = 0; kb < NKC; ++kb)   // P fragments: tokens in the permuted order
                     if (kb <= pkmax) acc = X::mma(op.p[kb], X::ld_perm(YT + rl * LDU + X::poff(kb, g)), acc);
                 // O tile through LDS, written as 16-byte pieces (a token's 16 state rows are
-                // sizeof(E) pieces)
+                // sizeof(E) pieces) with the nontemporal hint: o is written once and not read here
                 E* os = Os[w4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) os[(rq + j) * LDO + rl] = X::from_f(acc[j]);
@@ -1140,7 +1140,8 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
                 const uint4 v = *reinterpret_cast<const uint4*>(os + tok * LDO + piece * EPV);
                 const int t = t0 + m * 16 + tok;
                 if (lane < 16 * PPR && (!TAIL || t < T))
-                    *reinterpret_cast<uint4*>(og + ((size_t)b * p.Ts + p.t0 + t) * Hv * DV + piece * EPV) = v;
+                    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v),
+                                                reinterpret_cast<u32x4*>(og + ((size_t)b * p.Ts + p.t0 + t) * Hv * DV + piece * EPV));
             }
             lds_barrier();   // (B2)
         };
