@@ -58,15 +58,24 @@ struct DecodeTable {
     int qk_norm;
 };
 
+// Tiling of a decode workgroup (256 threads): LPR lanes per state row, RIT rows per pass of
+// the workgroup, RPB rows per workgroup (NIT passes, each thread's loads all in flight at once),
+// NBLK workgroups per (batch, value head).  Four passes instead of two measured the same.
+template <int DK, int DV>
+struct DecodeTiling {
+    static constexpr int LPR = DK / 4;
+    static constexpr int RIT = 256 / LPR;
+    static constexpr int RPB = (2 * RIT < DV) ? 2 * RIT : DV;
+    static constexpr int NIT = RPB / RIT;
+    static constexpr int NBLK = DV / RPB;
+};
+
 // One workgroup's share of a decode step: block `wg` of the B * Hv * NBLK blocks of p.
 template <typename E, int DK, int DV>
 __device__ __forceinline__ void decode_block(const DecodeParams& p, int wg) {
     using X = Elem<E>;
-    constexpr int LPR = DK / 4;
-    constexpr int RIT = 256 / LPR;
-    constexpr int RPB = (2 * RIT < DV) ? 2 * RIT : DV;
-    constexpr int NIT = RPB / RIT;
-    constexpr int NBLK = DV / RPB;
+    typedef DecodeTiling<DK, DV> Tl;
+    constexpr int LPR = Tl::LPR, RIT = Tl::RIT, RPB = Tl::RPB, NIT = Tl::NIT, NBLK = Tl::NBLK;
     static_assert(RIT <= DV && NIT * RIT == RPB && NBLK * RPB == DV, "decode tiling");
 
     const int blk = wg % NBLK;
@@ -136,8 +145,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 // own decode_kernel launch.
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) void decode_layers_kernel(DecodeTable t) {
-    constexpr int NBLK = DV / ((2 * (256 / (DK / 4)) < DV) ? 2 * (256 / (DK / 4)) : DV);
-    const int per = t.B * t.Hv * NBLK;
+    const int per = t.B * t.Hv * DecodeTiling<DK, DV>::NBLK;
     const int l = blockIdx.x / per;
     const DecodeLayerPtrs& lp = t.layer[l];
     DecodeParams p;
@@ -149,21 +157,13 @@ __global__ __launch_bounds__(256) void decode_layers_kernel(DecodeTable t) {
 
 template <typename E, int DK, int DV>
 inline hipError_t launch_decode_layers(const DecodeTable& t, hipStream_t stream) {
-    constexpr int LPR = DK / 4;
-    constexpr int RIT = 256 / LPR;
-    constexpr int RPB = (2 * RIT < DV) ? 2 * RIT : DV;
-    constexpr int NBLK = DV / RPB;
-    const dim3 grid((unsigned)(t.nlayers * t.B * t.Hv * NBLK));
+    const dim3 grid((unsigned)(t.nlayers * t.B * t.Hv * DecodeTiling<DK, DV>::NBLK));
     return launch_kernel(decode_layers_kernel<E, DK, DV>, grid, dim3(256), stream, t);
 }
 
 template <typename E, int DK, int DV>
 inline hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
-    constexpr int LPR = DK / 4;
-    constexpr int RIT = 256 / LPR;
-    constexpr int RPB = (2 * RIT < DV) ? 2 * RIT : DV;
-    constexpr int NBLK = DV / RPB;
-    dim3 grid((unsigned)(p.B * p.Hv * NBLK));
+    const dim3 grid((unsigned)(p.B * p.Hv * DecodeTiling<DK, DV>::NBLK));
     return launch_kernel(decode_kernel<E, DK, DV>, grid, dim3(256), stream, p);
 }
 
