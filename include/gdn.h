@@ -117,7 +117,8 @@ gdn_status gdn_prefill_qknorm(const void *q, const void *k, const void *v, const
 /* Flags of gdn_prefill_ex (bitwise or). */
 #define GDN_QK_NORM 1u         /* L2-normalise q and k inside, as gdn_prefill_qknorm         */
 #define GDN_PATH_SEQUENTIAL 2u /* token-sequential scan, state in registers (see below)     */
-#define GDN_PATH_AUTO 4u       /* sequential when T <= gdn_prefill_sequential_max_tokens(),
+#define GDN_PATH_AUTO 4u       /* the decode step for T == 1 from a given state, else the
+                                  sequential form when T <= gdn_prefill_sequential_max_tokens(),
                                   blockwise otherwise                                        */
 
 /* Prefill with a choice of evaluation form ("Optimizing on-device inference for Apple

@@ -140,11 +140,15 @@ gdn_status scratch_address(void** out) {
 
 namespace {
 
+// How a prefill call is evaluated once its arguments are checked: the blockwise form (the
+// workspace path), the token-sequential form, or (one token from a given state) the decode step.
+enum class Form { blockwise, sequential, decode_step };
+
 gdn_status prefill_stages(const void* q, const void* k, const void* v, const float* g,
                           const float* beta, const float* state_in, void* o, float* state_out,
                           int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype dtype,
                           void* workspace, size_t workspace_bytes, void* stream, int stages,
-                          int qk_norm, bool sequential, bool noalloc = false) {
+                          int qk_norm, Form form, bool noalloc = false) {
     const gdn_status sc = shape_check(B, T, Hk, Hv, dk, dv, chunk, dtype, true);
     if (sc != GDN_OK) return sc;
     if (!state_out) return GDN_ERR_NULL;
@@ -176,7 +180,14 @@ gdn_status prefill_stages(const void* q, const void* k, const void* v, const flo
         return gdn::copy_state(state_in, state_out, (size_t)B * Hv * dv * dk, st) == hipSuccess
                    ? GDN_OK : GDN_ERR_HIP;
     }
-    if (sequential) {   // the state stays in registers: no workspace, one launch
+    if (form == Form::decode_step) {   // (T == 1, state_in given) its layouts are the prefill's at T = 1
+        gdn::DecodeParams p;
+        p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.state_in = state_in;
+        p.state_out = state_out; p.o = o; p.B = B; p.Hk = Hk; p.Hv = Hv; p.qk_norm = qk_norm;
+        const hipError_t e = dtype == GDN_BF16 ? gdn::decode_bf16(dk, dv, p, st) : gdn::decode_f32(dk, dv, p, st);
+        return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    }
+    if (form == Form::sequential) {   // the state stays in registers: no workspace, one launch
         gdn::PrefillParams p{};
         p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.state_in = state_in;
         p.o = o; p.state_out = state_out;
@@ -271,7 +282,7 @@ gdn_status gdn_prefill(const void* q, const void* k, const void* v, const float*
                        int B, int T, int Hk, int Hv, int dk, int dv, int chunk, gdn_dtype dtype,
                        void* workspace, size_t workspace_bytes, void* stream) {
     return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
-                          dtype, workspace, workspace_bytes, stream, 3, 0, false);
+                          dtype, workspace, workspace_bytes, stream, 3, 0, Form::blockwise);
 }
 
 gdn_status gdn_prefill_ex(const void* q, const void* k, const void* v, const float* g,
@@ -282,20 +293,16 @@ gdn_status gdn_prefill_ex(const void* q, const void* k, const void* v, const flo
     if (flags & ~(unsigned)(GDN_QK_NORM | GDN_PATH_SEQUENTIAL | GDN_PATH_AUTO) ||
         ((flags & GDN_PATH_SEQUENTIAL) && (flags & GDN_PATH_AUTO)))
         return GDN_ERR_UNSUPPORTED;
-    bool seq = (flags & GDN_PATH_SEQUENTIAL) != 0;
-    if ((flags & GDN_PATH_AUTO) && T == 1 && state_in) {
-        // one token from a given state: the decode step, a single read and write of the state
-        // (its layouts are the prefill's at T = 1)
-        const gdn_status sc = shape_check(B, T, Hk, Hv, dk, dv, chunk, dtype, true);
-        if (sc != GDN_OK) return sc;
-        return (flags & GDN_QK_NORM)
-                   ? gdn_decode_step_qknorm(q, k, v, g, beta, state_in, state_out, o, B, Hk, Hv, dk, dv, dtype, stream)
-                   : gdn_decode_step(q, k, v, g, beta, state_in, state_out, o, B, Hk, Hv, dk, dv, dtype, stream);
+    Form form = (flags & GDN_PATH_SEQUENTIAL) ? Form::sequential : Form::blockwise;
+    if (flags & GDN_PATH_AUTO) {
+        // one token from a given state: the decode step, a single read and write of the state;
+        // else the sequential form up to the measured crossover
+        if (T == 1 && state_in) form = Form::decode_step;
+        else if (T <= gdn_prefill_sequential_max_tokens(B, Hk, Hv, dk, dv, dtype)) form = Form::sequential;
     }
-    if (flags & GDN_PATH_AUTO) seq = T <= gdn_prefill_sequential_max_tokens(B, Hk, Hv, dk, dv, dtype);
     return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
                           dtype, workspace, workspace_bytes, stream, 3,
-                          (flags & GDN_QK_NORM) ? 1 : 0, seq);
+                          (flags & GDN_QK_NORM) ? 1 : 0, form);
 }
 
 int gdn_prefill_sequential_max_tokens(int B, int Hk, int Hv, int dk, int dv, gdn_dtype dtype) {
@@ -309,7 +316,7 @@ gdn_status gdn_prefill_qknorm(const void* q, const void* k, const void* v, const
                               int chunk, gdn_dtype dtype, void* workspace,
                               size_t workspace_bytes, void* stream) {
     return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
-                          dtype, workspace, workspace_bytes, stream, 3, 1, false);
+                          dtype, workspace, workspace_bytes, stream, 3, 1, Form::blockwise);
 }
 
 gdn_status gdn_prefill_prepare(const void* q, const void* k, const void* v, const float* g,
@@ -318,7 +325,7 @@ gdn_status gdn_prefill_prepare(const void* q, const void* k, const void* v, cons
                                int chunk, gdn_dtype dtype, void* workspace,
                                size_t workspace_bytes, void* stream) {
     return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
-                          dtype, workspace, workspace_bytes, stream, 1, 0, false);
+                          dtype, workspace, workspace_bytes, stream, 1, 0, Form::blockwise);
 }
 
 gdn_status gdn_prefill_scan(const void* q, const void* k, const void* v, const float* g,
@@ -327,7 +334,7 @@ gdn_status gdn_prefill_scan(const void* q, const void* k, const void* v, const f
                             gdn_dtype dtype, void* workspace, size_t workspace_bytes,
                             void* stream) {
     return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
-                          dtype, workspace, workspace_bytes, stream, 2, 0, false);
+                          dtype, workspace, workspace_bytes, stream, 2, 0, Form::blockwise);
 }
 
 gdn_status gdn_prefill_noalloc(const void* q, const void* k, const void* v, const float* g,
@@ -335,7 +342,7 @@ gdn_status gdn_prefill_noalloc(const void* q, const void* k, const void* v, cons
                                int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                                gdn_dtype dtype, void* stream) {
     return prefill_stages(q, k, v, g, beta, state_in, o, state_out, B, T, Hk, Hv, dk, dv, chunk,
-                          dtype, nullptr, 0, stream, 3, 0, false, true);
+                          dtype, nullptr, 0, stream, 3, 0, Form::blockwise, true);
 }
 
 }  // extern "C"

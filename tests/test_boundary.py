@@ -127,15 +127,18 @@ def test_prefill_ex_rejects_flags(flags):
     assert rc == 3
 
 
+@pytest.mark.parametrize("T", [64, 1])   # T = 1 from a given state: GDN_PATH_AUTO's decode step
 @pytest.mark.parametrize("flags", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("kw,code", [(dict(q=None), 1), (dict(Hv=3), 2), (dict(dk=48), 3),
-                                     (dict(q=BASE + 2), 4), (dict(o=BASE + 10 * MB), 5)])
-def test_prefill_ex_validates_on_every_path(kw, code, flags):
-    a = dict(q=BASE, o=BASE + 60 * MB, Hv=4, dk=32)
+                                     (dict(q=BASE + 2), 4), (dict(o=BASE + 10 * MB), 5),
+                                     (dict(ws=BASE + 60 * MB), 5)])
+def test_prefill_ex_validates_on_every_path(kw, code, flags, T):
+    # every path checks the same arguments, the workspace (even where it goes unused) included
+    a = dict(q=BASE, o=BASE + 60 * MB, Hv=4, dk=32, ws=BASE + 100 * MB)
     a.update(kw)
     rc = gdn.lib().gdn_prefill_ex(a["q"], BASE + 10 * MB, BASE + 20 * MB, BASE + 40 * MB,
-                                  BASE + 41 * MB, BASE + 50 * MB, a["o"], BASE + 80 * MB, 1, 64,
-                                  2, a["Hv"], a["dk"], 32, 16, 0, BASE + 100 * MB, 1 << 26, None,
+                                  BASE + 41 * MB, BASE + 50 * MB, a["o"], BASE + 80 * MB, 1, T,
+                                  2, a["Hv"], a["dk"], 32, 16, 0, a["ws"], 1 << 26, None,
                                   flags)
     assert rc == code
 
