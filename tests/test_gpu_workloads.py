@@ -280,24 +280,34 @@ def test_prepare_then_scan_equals_one_call(dt):
     assert nrel(np32(oe), o_ref) < TOL_O and nrel(se.cpu().numpy(), s_ref) < TOL_S
 
 
-@pytest.mark.parametrize("dt,T", [(torch.bfloat16, 8292), (torch.float32, 12100)])
-def test_cache_sized_passes_equal_one_pass(dt, T):
-    # at 16/32 heads and d = 128 these prompts exceed one pass's last-level-cache budget, so
-    # gdn_prefill runs them in equal passes even with the one-pass workspace; the two stages
-    # called separately always make one pass: the results must be bitwise equal
-    d = to_dev(make_inputs(1, T, 16, 32, 128, 128, seed=27, state_std=0.1, dtype=dt))
-    nbytes = gdn.gdn_prefill_workspace_bytes(1, T, 16, 32, 128, 128, 64, dt)
+@pytest.mark.parametrize("dt,T,B", [(torch.bfloat16, 8292, 1), (torch.float32, 12100, 1),
+                                    (torch.bfloat16, 4100, 2)])
+def test_cache_sized_passes_equal_one_pass(dt, T, B):
+    # at 16/32 heads and d = 128 these prompts exceed one pass's last-level-cache budget (the
+    # batch of two at 4K too: the budget covers the whole batch), so gdn_prefill runs them in
+    # equal passes even with the one-pass workspace; the two stages called separately always
+    # make one pass: the results must be bitwise equal
+    h = make_inputs(B, T, 16, 32, 128, 128, seed=27 + B, state_std=0.1, dtype=dt)
+    d = to_dev(h)
+    nbytes = gdn.gdn_prefill_workspace_bytes(B, T, 16, 32, 128, 128, 64, dt)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     o1, o2 = torch.empty_like(d["v"]), torch.empty_like(d["v"])
-    s1 = torch.empty((1, 32, 128, 128), dtype=torch.float32, device="cuda")
+    s1 = torch.empty((B, 32, 128, 128), dtype=torch.float32, device="cuda")
     s2 = torch.empty_like(s1)
-    say("cache-sized passes", dt, T)
+    say("cache-sized passes", dt, T, B)
     args = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"])
     gdn.gdn_prefill(*args, o1, s1, 64, ws)
     gdn.gdn_prefill_prepare(*args, o2, s2, 64, ws)
     gdn.gdn_prefill_scan(*args, o2, s2, 64, ws)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    if B > 1:   # and the batch against the oracle, every (batch, value head)
+        o_ref, s_ref = oracle_prefill(h, h["state"], nthreads=NTHREADS)
+        og, sg = np32(o1), s1.cpu().numpy()
+        for b in range(B):
+            for hv in range(32):
+                eo, es = nrel(og[b, :, hv], o_ref[b, :, hv]), nrel(sg[b, hv], s_ref[b, hv])
+                assert eo < TOL_O and es < TOL_S, (b, hv, eo, es)
 
 
 def test_long_128k_bounded_workspace(c4):
