@@ -140,24 +140,25 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     decode_block<E, DK, DV>(p, blockIdx.x);
 }
 
-// The same step over t.nlayers layers in one launch: workgroup w takes block w % per of layer
-// w / per (per = B * Hv * NBLK), so every layer's state is read and written exactly as by its
-// own decode_kernel launch.
+// The same step over t.nlayers layers in one launch: workgroup (w, l) of the 2-D grid takes
+// block w of layer l, so every layer's state is read and written exactly as by its own
+// decode_kernel launch (the layer index needs no division by sizes loaded from the arguments,
+// so the layer's pointers are fetched at once).
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) void decode_layers_kernel(DecodeTable t) {
-    const int per = t.B * t.Hv * DecodeTiling<DK, DV>::NBLK;
-    const int l = blockIdx.x / per;
+    const int l = blockIdx.y;
+    const int w = blockIdx.x;
     const DecodeLayerPtrs& lp = t.layer[l];
     DecodeParams p;
     p.q = lp.q; p.k = lp.k; p.v = lp.v; p.g = lp.g; p.beta = lp.beta;
     p.state_in = lp.state_in; p.state_out = lp.state_out; p.o = lp.o;
     p.B = t.B; p.Hk = t.Hk; p.Hv = t.Hv; p.qk_norm = t.qk_norm;
-    decode_block<E, DK, DV>(p, blockIdx.x - l * per);
+    decode_block<E, DK, DV>(p, w);
 }
 
 template <typename E, int DK, int DV>
 inline hipError_t launch_decode_layers(const DecodeTable& t, hipStream_t stream) {
-    const dim3 grid((unsigned)(t.nlayers * t.B * t.Hv * DecodeTiling<DK, DV>::NBLK));
+    const dim3 grid((unsigned)(t.B * t.Hv * DecodeTiling<DK, DV>::NBLK), (unsigned)t.nlayers);
     return launch_kernel(decode_layers_kernel<E, DK, DV>, grid, dim3(256), stream, t);
 }
 
