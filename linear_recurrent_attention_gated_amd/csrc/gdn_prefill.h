@@ -816,7 +816,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // residual Y = V - diag(Gamma) K S^T for their 16-token tile, then S^T <- Gamma_n S^T + Z Y for
 // their state tiles.  Output waves 4..7 compute O = Gamma (Q S^T) + P' Y for their token tile
 // one barrier behind, from a double-buffered copy of the state, so the output products stay
-// off the chain, and write O as 16-byte pieces staged through LDS.  Each role prefetches its own
+// off the chain; they form the tile transposed, so that each lane holds four consecutive state
+// rows of one token and stores them from the accumulator.  Each role prefetches its own
 // operands NB chunks ahead into registers; the chain waves issue those loads just before the
 // barriers they would wait at anyway, not between a barrier and the next chunk's products.
 // SPLIT: feed the state to K S^T as a bf16 hi + lo pair (two MFMAs) so the residual Y sees
@@ -851,7 +852,7 @@ struct OutputOperands {
     static constexpr int NKC = (C + X::KB - 1) / X::KB;
     frag q[NKD];
     frag p[NKC];
-    f32x4 gr;     // output scale of this lane's four token rows
+    float gr;     // output scale of this lane's token
 };
 
 template <typename E, int DK, int DV, int C, bool SPLIT>
@@ -875,8 +876,6 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
     __shared__ __align__(16) E Sb[2][16 * LDS_];              // state slice, hi part, 2 buffers
     __shared__ __align__(16) E Sl[2][SPLIT ? 16 * LDS_ : EPV];  // lo part
     __shared__ __align__(16) E YT[16 * LDU];                   // Y^T (for Z Y and P' Y)
-    constexpr int LDO = 16 + EPV;
-    __shared__ __align__(16) E Os[4][16 * LDO];                // output tile staging, per output wave
 
     // XCD-aware placement: consecutive workgroups go to different XCDs; place the slices of
     // one head on the same XCD so they share its L2 for the head's chunk operands.
@@ -1090,7 +1089,7 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
 
         auto fetch = [&](OOps& op, int c) {
             const int t0 = c * C;
-            op.gr = *reinterpret_cast<const f32x4*>(gates + (size_t)c * Sh::GATES + m * 16 + rq);
+            op.gr = gates[(size_t)c * Sh::GATES + m * 16 + rl];
             const E* qsrc = qfg + (size_t)c * Sh::W_PER_CHUNK;
 #pragma unroll
             for (int kb = 0; kb < NKD; kb += X::GRP) X::ld_grp(qsrc + X::foff(kb, lane), &op.q[kb]);
@@ -1115,6 +1114,11 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
             if (has_tile) {
                 const E* sr = &Sb[c & 1][rl * LDS_];
                 const bool qok = !TAIL || (t0 + m * 16 + rl < T);
+                // The output tile transposed, O^T = S Q^T + Y^T P'^T: the same fragments as operands
+                // in the other order (the state rows and Y rows as A, the Q and P' rows as B), so
+                // that lane (g, t) ends with the state rows rq..rq+3 of token t -- contiguous in o
+                // and stored from the accumulator directly, with the nontemporal hint (o is
+                // written once and not read here)
                 f32x4 accq = zero4();
 #pragma unroll
                 for (int kb = 0; kb < NKD; kb += X::GRP) {
@@ -1122,26 +1126,23 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
                     X::ld_grp(sr + X::doff(kb, g), sh);
 #pragma unroll
                     for (int i = 0; i < X::GRP; ++i)
-                        accq = X::mma(TAIL ? X::keep_if(op.q[kb + i], qok) : op.q[kb + i], sh[i], accq);
+                        accq = X::mma(sh[i], TAIL ? X::keep_if(op.q[kb + i], qok) : op.q[kb + i], accq);
                 }
                 f32x4 acc = accq * op.gr;
 #pragma unroll
                 for (int kb = 0; kb < NKC; ++kb)   // P fragments: tokens in the permuted order
-                    if (kb <= pkmax) acc = X::mma(op.p[kb], X::ld_perm(YT + rl * LDU + X::poff(kb, g)), acc);
-                // O tile through LDS, written as 16-byte pieces (a token's 16 state rows are
-                // sizeof(E) pieces) with the nontemporal hint: o is written once and not read here
-                E* os = Os[w4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) os[(rq + j) * LDO + rl] = X::from_f(acc[j]);
-                wave_lds_sync();
-                constexpr int PPR = (int)sizeof(E);
-                // lanes past the tile's 16 rows (bf16: lanes 32..63) read row tok & 15 and store nothing
-                const int tok = (lane / PPR) & 15, piece = lane % PPR;
-                const uint4 v = *reinterpret_cast<const uint4*>(os + tok * LDO + piece * EPV);
-                const int t = t0 + m * 16 + tok;
-                if (lane < 16 * PPR && (!TAIL || t < T))
-                    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v),
-                                                reinterpret_cast<u32x4*>(og + ((size_t)b * p.Ts + p.t0 + t) * Hv * DV + piece * EPV));
+                    if (kb <= pkmax) acc = X::mma(X::ld_perm(YT + rl * LDU + X::poff(kb, g)), op.p[kb], acc);
+                const int t = t0 + m * 16 + rl;
+                if (!TAIL || t < T) {
+                    E* dst = og + ((size_t)b * p.Ts + p.t0 + t) * Hv * DV + rq;
+                    if constexpr (sizeof(E) == 2) {
+                        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                        const u32x2 w = {f2bf2(acc[0], acc[1]), f2bf2(acc[2], acc[3])};
+                        __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(dst));
+                    } else {
+                        __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(dst));
+                    }
+                }
             }
             lds_barrier();   // (B2)
         };
