@@ -816,8 +816,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // residual Y = V - diag(Gamma) K S^T for their 16-token tile, then S^T <- Gamma_n S^T + Z Y for
 // their state tiles.  Output waves 4..7 compute O = Gamma (Q S^T) + P' Y for their token tile
 // one barrier behind, from a double-buffered copy of the state, so the output products stay
-// off the chain; they form the tile transposed, so that each lane holds four consecutive state
-// rows of one token and stores them from the accumulator.  Each role prefetches its own
+// off the chain.  Both roles form their token tiles transposed (state rows by tokens), so that
+// each lane holds four consecutive state rows of one token: 8 contiguous bytes of v to read or
+// of o to write (16 in fp32).  Each role prefetches its own
 // operands NB chunks ahead into registers; the chain waves issue those loads just before the
 // barriers they would wait at anyway, not between a barrier and the next chunk's products.
 // SPLIT: feed the state to K S^T as a bf16 hi + lo pair (two MFMAs) so the residual Y sees
@@ -840,7 +841,7 @@ struct ChainOperands {
     static constexpr int NKC = (C + X::KB - 1) / X::KB;
     frag kf[NKD];       // K row tile (rows tokens, k = dk)
     frag z[TPW][NKC];   // Z rows of this wave's state tiles (rows dk, k = tokens; permuted)
-    f32x4 gk;           // key-row scale of this lane's four token rows
+    float gk;           // key-row scale of this lane's token row
     float gn;           // chunk decay exp(gamma_last)
 };
 
@@ -911,8 +912,8 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
         const E* KFg = reinterpret_cast<const E*>(p.KF) + ((size_t)b * Hk + hk) * N * Sh::W_PER_CHUNK
                        + (size_t)m * NKD * Sh::FRAG;
         const E* Zg = reinterpret_cast<const E*>(p.Z) + (size_t)bh * N * Sh::Z_PER_CHUNK;
-        // v of this lane's state row (i0 + rl) for token rows rq + [0, 4) of tile m
-        const E* vg = reinterpret_cast<const E*>(p.v) + (size_t)h * DV + i0 + rl;
+        // v of this lane's token row (rl) of tile m, state rows i0 + rq + [0, 4)
+        const E* vg = reinterpret_cast<const E*>(p.v) + (size_t)h * DV + i0 + rq;
 
         // a later chunk's operands are fetched in parts, each issued where its registers are
         // free and this wave would otherwise wait: K rows and the key-row scales once Y is
@@ -920,15 +921,21 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
         // and the decay once the update has read them (before the second)
         auto fetch_w = [&](COps& op, int c) {
             const float* gc = gates + (size_t)c * Sh::GATES;
-            op.gk = *reinterpret_cast<const f32x4*>(gc + C + m * 16 + rq);
+            op.gk = gc[C + m * 16 + rl];
             const E* ksrc = KFg + (size_t)c * Sh::W_PER_CHUNK;
 #pragma unroll
             for (int kb = 0; kb < NKD; kb += X::GRP) X::ld_grp(ksrc + X::foff(kb, lane), &op.kf[kb]);
         };
         auto fetch_v = [&](E (&v)[4], int c) {
-            const int tb = c * C + m * 16 + rq;   // rows past the prompt read its last token
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = vg[((size_t)b * p.Ts + p.t0 + min(tb + j, T - 1)) * Hv * DV];
+            const int tb = min(c * C + m * 16 + rl, T - 1);   // rows past the prompt read its last token
+            const E* src = vg + ((size_t)b * p.Ts + p.t0 + tb) * Hv * DV;
+            if constexpr (sizeof(E) == 2) {
+                const uint2 u = *reinterpret_cast<const uint2*>(src);
+                __builtin_memcpy(v, &u, 8);
+            } else {
+                const float4 u = *reinterpret_cast<const float4*>(src);
+                __builtin_memcpy(v, &u, 16);
+            }
         };
         auto fetch_k = [&](COps& op, int c) {
             const float* gc = gates + (size_t)c * Sh::GATES;
@@ -985,17 +992,21 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
                     X::ld_grp(sr + X::doff(kb, g), &sh[kb]);
                     if (SPLIT) X::ld_grp(sl + X::doff(kb, g), &slo[kb]);
                 }
+                // (K S^T)^T = S K^T: the state rows as A and the K rows as B (the same fragments
+                // in the other operand order), so that lane (g, t) ends with the state rows
+                // rq..rq+3 of token t, whose v is 8 (fp32: 16) contiguous bytes
                 f32x4 acc = zero4(), accl = zero4();
 #pragma unroll
                 for (int kb = 0; kb < NKD; ++kb) {
-                    acc = X::mma(op.kf[kb], sh[kb], acc);
-                    if (SPLIT) accl = X::mma(op.kf[kb], slo[kb], accl);
+                    acc = X::mma(sh[kb], op.kf[kb], acc);
+                    if (SPLIT) accl = X::mma(slo[kb], op.kf[kb], accl);
                 }
                 if (SPLIT) acc += accl;
                 E y[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) y[j] = X::from_f(X::to_f(v[j]) - op.gk[j] * acc[j]);
-                store4(YT + rl * LDU + m * 16 + rq, y);
+                for (int j = 0; j < 4; ++j) y[j] = X::from_f(X::to_f(v[j]) - op.gk * acc[j]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) YT[(rq + j) * LDU + m * 16 + rl] = y[j];
             }
             if (PF) fetch_w(op, nc);
             lds_barrier();   // (B1) Y complete; chunk c's slice was read from buffer cur
