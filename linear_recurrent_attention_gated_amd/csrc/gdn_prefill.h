@@ -1147,7 +1147,6 @@ __global__ __launch_bounds__(kScanThreads) void inter_chunk_kernel(PrefillParams
                 if (!TAIL || t < T) {
                     E* dst = og + ((size_t)b * p.Ts + p.t0 + t) * Hv * DV + rq;
                     if constexpr (sizeof(E) == 2) {
-                        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
                         const u32x2 w = {f2bf2(acc[0], acc[1]), f2bf2(acc[2], acc[3])};
                         __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(dst));
                     } else {
