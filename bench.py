@@ -23,7 +23,9 @@ a 1 GiB flush fill (one call between two events), the two kernels timed as the t
 (gdn_prefill_prepare, then gdn_prefill_scan) with an event between them, warm-cache stages,
 the fused-normalisation and all-fp32 calls, the 131072-token long-memory prompt (gdn_prefill,
 which runs it in passes sized to the last-level cache, against one pass over the whole prompt),
-and a plain device copy as the achievable-bandwidth reference.  The CPU oracle runs on the host on the same prefill workload,
+and a plain device copy as the achievable-bandwidth reference.  The HBM bytes and the
+matrix-core work per launch come from rocprofv3 counter runs of this script, summarised into
+profiles/ (--summarize-counters, --summarize-mfma) and used while the kernel sources are unchanged.  The CPU oracle runs on the host on the same prefill workload,
 alternating with cold GPU calls (its output doubles as a parity check of the GPU output).
 """
 import argparse
@@ -91,35 +93,46 @@ def load_traffic():
     return out
 
 
+def _kernel_key(name, grid_size):
+    """The key under which a dispatch's counters are summarised.  The bench also runs the
+    fused-normalisation and all-fp32 prefills: their kernels are other template instances, kept
+    apart by name; decode launches by their number of layers (grid size)."""
+    el = "f32" if "<float" in name else "bf16"
+    if "copybuffer" in name.lower():
+        return "copy"
+    if "inter_chunk_kernel" in name:
+        return "inter" if el == "bf16" else "inter_f32"
+    if "intra_chunk_kernel" in name:
+        return ("intra_qknorm" if ", true>" in name else "intra") + ("" if el == "bf16" else "_f32")
+    if "decode_layers_kernel" in name:
+        return "decode_layers_L%d" % (int(float(grid_size or "0")) // (256 * 256))
+    if "decode_kernel" in name:
+        return "decode_L%d" % (int(float(grid_size or "0")) // (256 * 256))
+    return None
+
+
+def _counter_rows(d, counters):
+    """(key, counter, value) of every dispatch in the rocprofv3 CSV output under d."""
+    import csv
+    import glob
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") not in counters:
+                    continue
+                key = _kernel_key(row.get("Kernel_Name", ""), row.get("Grid_Size"))
+                if key is not None:
+                    yield key, row["Counter_Name"], float(row["Counter_Value"])
+
+
 def summarize_counters(fetch_dir, write_dir):
     """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel from rocprofv3 CSV output,
     scaled by what the same counters read for a plain copy of COPY_CALIBRATION_BYTES."""
-    import csv
-    import glob
 
     def per_kernel(d, counter):
         sums = {}
-        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            with open(path) as fh:
-                for row in csv.DictReader(fh):
-                    if row.get("Counter_Name") != counter:
-                        continue
-                    name = row.get("Kernel_Name", "")
-                    # the bench also runs the fused-normalisation and all-fp32 prefills: their
-                    # kernels are other template instances, kept apart by name
-                    el = "f32" if "<float" in name else "bf16"
-                    key = ("copy" if "copybuffer" in name.lower()
-                           else ("inter" if el == "bf16" else "inter_f32")
-                           if "inter_chunk_kernel" in name
-                           else ("intra_qknorm" if ", true>" in name else "intra") + ("" if el == "bf16" else "_f32")
-                           if "intra_chunk_kernel" in name
-                           else "decode_L%d" % (int(float(row.get("Grid_Size", "0"))) // (256 * 256))
-                           if "decode_kernel" in name
-                           else "decode_layers_L%d" % (int(float(row.get("Grid_Size", "0"))) // (256 * 256))
-                           if "decode_layers_kernel" in name else None)
-                    if key is None:
-                        continue
-                    sums.setdefault(key, []).append(float(row["Counter_Value"]) * 1024.0)
+        for key, _, value in _counter_rows(d, (counter,)):
+            sums.setdefault(key, []).append(value * 1024.0)
         # the calibration copy is the largest copy; small copies are runtime housekeeping
         return {k: (max(v) if k == "copy" else sum(v) / len(v)) for k, v in sums.items()}
 
@@ -155,6 +168,75 @@ def summarize_counters(fetch_dir, write_dir):
     print("\n".join(lines))
 
 
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_counters.txt")
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32",
+                 "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+MI355X_XCDS, MI355X_SIMDS = 8, 1024
+
+
+def summarize_mfma(d):
+    """Matrix-core work per dispatch and kernel from one rocprofv3 --pmc run of MFMA_COUNTERS:
+    FLOPs = MOPS x 512 (rocprofv3's MfmaFlops metrics), and the busy fraction = MFMA busy cycles
+    summed over the SIMDs / (active cycles x SIMDs) (its MfmaUtil metric).  GRBM_GUI_ACTIVE
+    comes summed over the XCDs, each of which counts the dispatch's active cycles."""
+    sums = {}
+    for key, counter, value in _counter_rows(d, MFMA_COUNTERS):
+        sums.setdefault((key, counter), []).append(value)
+    avg = {k: sum(v) / len(v) for k, v in sums.items()}
+    keys = sorted({k for k, _ in avg if k != "copy"})
+    lines = ["# Matrix-core work per dispatch (rocprofv3 counters %s), made by:" % ", ".join(MFMA_COUNTERS),
+             "#   rocprofv3 --pmc %s --output-format csv -d %s -o mfma -- "
+             "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --skip-long" % (" ".join(MFMA_COUNTERS), d),
+             "#   python bench.py --summarize-mfma %s" % d,
+             "# *_flops_bf16 / *_flops_f32: MOPS x 512; *_busy_frac: MFMA busy cycles over (active",
+             "# cycles per XCD x %d SIMDs); keys as in hbm_traffic.txt." % MI355X_SIMDS,
+             "source_hash: %s" % kernel_source_hash()]
+    for k in keys:
+        fb = avg.get((k, "SQ_INSTS_VALU_MFMA_MOPS_BF16"), 0.0) * 512
+        ff = avg.get((k, "SQ_INSTS_VALU_MFMA_MOPS_F32"), 0.0) * 512
+        busy = avg.get((k, "SQ_VALU_MFMA_BUSY_CYCLES"), 0.0)
+        active = avg.get((k, "GRBM_GUI_ACTIVE"), 0.0) / MI355X_XCDS
+        lines += ["%s_flops_bf16: %.0f" % (k, fb), "%s_flops_f32: %.0f" % (k, ff),
+                  "%s_busy_frac: %.4f" % (k, busy / (active * MI355X_SIMDS) if active else 0.0)]
+    pf = [avg.get((k, "SQ_INSTS_VALU_MFMA_MOPS_BF16"), 0.0) * 512 for k in ("intra", "inter")]
+    pf32 = [avg.get((k, "SQ_INSTS_VALU_MFMA_MOPS_F32"), 0.0) * 512 for k in ("intra", "inter")]
+    lines += ["prefill_flops_bf16_per_launch: %.0f" % sum(pf),
+              "prefill_flops_f32_per_launch: %.0f" % sum(pf32)]
+    with open(MFMA_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def load_mfma():
+    """The MFMA counter summary (profiles/mfma_counters.txt) while the kernel sources are
+    unchanged since it was taken, else None."""
+    try:
+        with open(MFMA_FILE) as fh:
+            doc = dict(l.split(":", 1) for l in fh.read().splitlines() if ":" in l and not l.startswith("#"))
+    except (OSError, ValueError):
+        return None
+    doc = {k.strip(): v.strip() for k, v in doc.items()}
+    if doc.get("source_hash") != kernel_source_hash():
+        return None
+    return {k: float(v) for k, v in doc.items() if k != "source_hash"}
+
+
+def mfma_counter_fields(doc, call_us):
+    """The prefill's matrix-core work as the counters measured it (profiles/mfma_counters.txt):
+    FLOPs executed per call on the bf16 and fp32 matrix cores, their rate over the call's
+    measured duration against the bf16 peak, and each kernel's matrix-core busy fraction."""
+    if not doc:
+        return None
+    fb, ff = doc.get("prefill_flops_bf16_per_launch", 0.0), doc.get("prefill_flops_f32_per_launch", 0.0)
+    tflops = (fb + ff) / (call_us * 1e-6) / 1e12
+    return {"source": "profiles/mfma_counters.txt (SQ_INSTS_VALU_MFMA_MOPS_BF16/_F32 x 512, "
+                      "SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE)",
+            "gflop_bf16_per_call": round(fb / 1e9, 3), "gflop_f32_per_call": round(ff / 1e9, 3),
+            "achieved_tflops": round(tflops, 2),
+            "frac_of_bf16_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "busy_frac_intra": doc.get("intra_busy_frac"), "busy_frac_inter": doc.get("inter_busy_frac")}
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +255,9 @@ def parse():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script "
                          "with --copy-calibration into profiles/hbm_traffic.txt, then exit")
+    ap.add_argument("--summarize-mfma", metavar="MFMA_DIR",
+                    help="turn a rocprofv3 --pmc run of the MFMA counters (op counts, busy cycles, "
+                         "active cycles) of this script into profiles/mfma_counters.txt, then exit")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="turn a rocprofv3 --kernel-trace run of this script (with --no-cpu-baseline "
                          "and the same --steps / --warmup) into the per-phase kernel table in "
@@ -442,6 +527,9 @@ def main():
     args = parse()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.warmup, args.steps, args.trace_bench_out)
@@ -778,6 +866,7 @@ def main():
                 "mtok_s_one_pass": round(LONG_128K.T / long_one_us, 2)},
             "mfma_tflops": round(pf_flops / (mean_pf * 1e-6) / 1e12, 2),
             "mfma_frac": round(pf_flops / (mean_pf * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "mfma_counters": mfma_counter_fields(load_mfma(), mean_pf),
         },
         "roofline": {
             "kernel": "gdn_prefill = intra_chunk_kernel then inter_chunk_kernel (mean duration "
