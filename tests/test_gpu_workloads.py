@@ -200,6 +200,22 @@ def test_single_token_prefill_equals_decode():
     assert nrel(np32(o_p[:, 0]), np32(o_d)) < TOL_O
 
 
+def test_many_workgroups_large_batch():
+    # 16 prompts of 96 tokens (a ragged second chunk) at 16/32 heads: 4,096 scan workgroups and
+    # 1,024 intra items, so the XCD-aware placement and the persistent intra grid run far past
+    # one workgroup per CU; sampled (batch, value head) pairs against the oracle
+    B, T = 16, 96
+    h = make_inputs(B, T, 16, 32, 128, 128, seed=29, state_std=0.2)
+    say("many workgroups", B, T)
+    o, s = gpu_prefill(h, 64, state=h["state"])
+    pairs = [(0, 0), (3, 7), (7, 31), (8, 16), (12, 5), (15, 30)]
+    o_ref, s_ref = oracle_prefill(h, h["state"], pairs=pairs, nthreads=NTHREADS)
+    og, sg = np32(o), s.cpu().numpy()
+    for i, (b, hv) in enumerate(pairs):
+        eo, es = nrel(og[b, :, hv], o_ref[i]), nrel(sg[b, hv], s_ref[i])
+        assert eo < TOL_O and es < TOL_S, (b, hv, eo, es)
+
+
 def test_shared_key_heads_equal_duplicated_heads_bitwise():
     d = make_inputs(1, 200, 16, 32, 128, 128, seed=24)
     dup = dict(d)
