@@ -598,10 +598,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int q = 0; q < NT / 2; ++q) {
             const int lo = 32 * q, hi = lo + 16;
+            // k runs in the order 4 g + kb (as in the accumulator tiles), so that a lane's four
+            // A values are one 16-byte run and the B reads of a k-step fall on distinct banks
             f32x4 t = zero4();
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
-                t = mma4(sR[(hi + rl) * LDR + lo + 4 * kb + g], sR[(lo + 4 * kb + g) * LDR + lo + rl], t);
+                t = mma4(sR[(hi + rl) * LDR + lo + 4 * g + kb], sR[(lo + 4 * g + kb) * LDR + lo + rl], t);
             f32x4 r21 = zero4();
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) r21 = mma4(sR[(hi + rl) * LDR + hi + 4 * g + kb], t[kb], r21);
@@ -648,14 +650,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if constexpr (NT == 4) {
         if (wave < 2) {
             const int tj = wave;   // tile column of T and R21
-            // T = A21 R11 (32 x 32, column tile tj); R11 is zero above its diagonal
+            // T = A21 R11 (32 x 32, column tile tj); R11 is zero above its diagonal; k in the
+            // order 16 blk + 4 g + kb, as in the first level
             f32x4 t0v = zero4(), t1v = zero4();
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb) {
-                if (kb >= 4 * tj) {
-                    const float bv = sR[(4 * kb + g) * LDR + tj * 16 + rl];
-                    t0v = mma4(sR[(32 + rl) * LDR + 4 * kb + g], bv, t0v);
-                    t1v = mma4(sR[(48 + rl) * LDR + 4 * kb + g], bv, t1v);
+            for (int blk = 0; blk < 2; ++blk) {
+                if (blk >= tj) {
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb) {
+                        const int k = 16 * blk + 4 * g + kb;
+                        const float bv = sR[k * LDR + tj * 16 + rl];
+                        t0v = mma4(sR[(32 + rl) * LDR + k], bv, t0v);
+                        t1v = mma4(sR[(48 + rl) * LDR + k], bv, t1v);
+                    }
                 }
             }
             // R21 = -R22 T; R22 rows 32..47 see T rows 0..15, rows 48..63 all of T
