@@ -549,17 +549,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
     }
     if (wave == 0) {
-        f32x4 Gd[NT], G1[NT / 2 > 0 ? NT / 2 : 1];
+        f32x4 Gd[NT];
 #pragma unroll
         for (int d = 0; d < NT; ++d) Gd[d] = kk_tile(d, d);
-#pragma unroll
-        for (int q = 0; q < NT / 2; ++q) G1[q] = kk_tile(2 * q + 1, 2 * q);
         p_row(0);
         store_rows(0);
 #pragma unroll
         for (int d = 0; d < NT; ++d) mask_a(d, d, Gd[d]);
-#pragma unroll
-        for (int q = 0; q < NT / 2; ++q) mask_a(2 * q + 1, 2 * q, G1[q]);
         wave_lds_sync();
         // (I + A_dd)^-1 of each 16x16 diagonal block by forward substitution: lane (d, j)
         // computes column j of block d
@@ -593,10 +589,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 *reinterpret_cast<float4*>(At + 4 * r4) =
                     make_float4(bs * x[4 * r4], bs * x[4 * r4 + 1], bs * x[4 * r4 + 2], bs * x[4 * r4 + 3]);
         }
-        wave_lds_sync();
-        // first doubling level: R21 = -R22 (A21 R11) for the block pairs (2q, 2q + 1)
-#pragma unroll
-        for (int q = 0; q < NT / 2; ++q) {
+    } else {
+        if (has_prow) {
+            p_row(pm);
+            store_rows(pm);
+        }
+        // the A21 tiles of the 32x32 diagonal blocks (2q + 1, 2q): q = 0 on wave 1, q = 1 on wave 3
+        if ((NT >= 2 && wave == 1) || (NT == 4 && wave == 3)) {
+            const int q = wave >> 1;
+            mask_a(2 * q + 1, 2 * q, kk_tile(2 * q + 1, 2 * q));
+        }
+        if (NT == 4 && wave >= 2) {   // the 32x32 off-diagonal block, one tile column per wave
+            const int tn = wave - 2;
+            const f32x4 Ga = kk_tile(2, tn), Gb = kk_tile(3, tn);
+            mask_a(2, tn, Ga);
+            mask_a(3, tn, Gb);
+        }
+        // the zeros of (R diag(beta))^T: row s, tokens r of earlier 16-token blocks (R is lower
+        // triangular) and past the chunk (phase 4 reads whole rows)
+        constexpr int CV = CP / 4;
+        for (int e = tid - 64; e < C * CV; e += kThreads - 64) {
+            const int s = e / CV, r4 = (e % CV) * 4;
+            if ((r4 >> 4) < (s >> 4) || r4 >= C)
+                *reinterpret_cast<float4*>(sRT + s * LDR + r4) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    if constexpr (NT >= 2) {
+        lds_barrier();   // (B2a) diagonal blocks inverted, A21 tiles masked
+        // first doubling level, R21 = -R22 (A21 R11), one block pair (2q, 2q + 1) per wave 2 + q
+        if (wave >= 2 && wave - 2 < NT / 2) {
+            const int q = wave - 2;
             const int lo = 32 * q, hi = lo + 16;
             // k runs in the order 4 g + kb (as in the accumulator tiles), so that a lane's four
             // A values are one 16-byte run and the B reads of a k-step fall on distinct banks
@@ -613,25 +635,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             const float bs = -sbeta[lo + rl];
             *reinterpret_cast<float4*>(sRT + (lo + rl) * LDR + hi + rq) =
                 make_float4(bs * r21[0], bs * r21[1], bs * r21[2], bs * r21[3]);
-        }
-    } else {
-        if (has_prow) {
-            p_row(pm);
-            store_rows(pm);
-        }
-        if (NT == 4 && wave >= 2) {   // the 32x32 off-diagonal block, one tile column per wave
-            const int tn = wave - 2;
-            const f32x4 Ga = kk_tile(2, tn), Gb = kk_tile(3, tn);
-            mask_a(2, tn, Ga);
-            mask_a(3, tn, Gb);
-        }
-        // the zeros of (R diag(beta))^T: row s, tokens r of earlier 16-token blocks (R is lower
-        // triangular) and past the chunk (phase 4 reads whole rows)
-        constexpr int CV = CP / 4;
-        for (int e = tid - 64; e < C * CV; e += kThreads - 64) {
-            const int s = e / CV, r4 = (e % CV) * 4;
-            if ((r4 >> 4) < (s >> 4) || r4 >= C)
-                *reinterpret_cast<float4*>(sRT + s * LDR + r4) = make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
     // fp32: the next item's Q rows (and v lines) are loaded here, after the branches of phase 2
